@@ -1,0 +1,207 @@
+/*
+ * gkv.h - C ABI of libgkv: shared-prefix decode attention over a contiguous
+ * HOT prefix pool and a token-level COLD suffix pool, for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operations follow the GraniKV pages ("GraniKV: Asymmetric Granularity
+ * KV-Cache Paging for Multi-Agent Systems with Long Shared Prefix"):
+ *   - paperlayer.ai summary §3 "Asymmetric KV-cache paging": shared prefixes
+ *     live contiguously in a HOT pool, suffix and decoded tokens one token per
+ *     slot in a COLD pool;
+ *   - reading card (observer.broadside.tech) "Key ideas": one bump-pointer
+ *     slab per prefix node in HOT, a token-level free list in COLD;
+ *   - paperlayer.ai Appendix B.8 (first-fit packing of mixed slab sizes) and
+ *     B.10 (HOT-first admission, failure when no contiguous extent fits, no
+ *     demotion);
+ *   - paperlayer.ai §2 "Prefix-suffix attention": prefix attention and suffix
+ *     attention are computed apart and joined by log-sum-exp;
+ *   - paperlayer.ai §3 "Per-step dispatch" and Appendix B.4: each step picks
+ *     the dense (batched GEMM) or the cascade prefix backend from
+ *     M_eff = B * n_q / n_kv against a measured threshold M_sat.
+ *
+ * Conventions
+ *   - Every function returns a gkv_status (0 = success) except gkv_destroy and
+ *     gkv_last_error.  No C++ exception crosses this boundary.  On failure the
+ *     context keeps a message readable with gkv_last_error.
+ *   - Device memory is owned by the caller (allocated by any means, e.g.
+ *     torch); the library never frees it.  "dev" marks device pointers,
+ *     "host" host pointers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls enqueue work and return without synchronising.
+ *   - Pool bookkeeping calls are host-only and synchronous.  A context is not
+ *     thread-safe; callers serialise calls on one context.  Device calls that
+ *     share a context's workspace must be issued on one stream (or otherwise
+ *     ordered), because each call reuses the workspace.
+ *   - Element types: GKV_F32 (float) or GKV_BF16 (bfloat16, round to nearest
+ *     even on output).  All arithmetic accumulates in fp32.
+ */
+#ifndef GKV_H
+#define GKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GKV_OK = 0,
+  GKV_ERR_INVALID = -1,   /* bad argument, shape, id or state */
+  GKV_ERR_NOSPACE = -2,   /* pool has no room; nothing changed */
+  GKV_ERR_NOTFOUND = -3,  /* unknown prefix id or unallocated slot; nothing changed */
+  GKV_ERR_DEVICE = -4     /* a HIP call failed (message names it) */
+} gkv_status;
+
+enum { GKV_F32 = 0, GKV_BF16 = 1 };
+
+enum {
+  GKV_BACKEND_AUTO = 0,     /* per step: dense iff M_eff >= m_sat */
+  GKV_BACKEND_CASCADE = 1,  /* split-K prefix kernel reading each slab once */
+  GKV_BACKEND_DENSE = 2     /* M-tiled batched-GEMM prefix kernel (bf16 only) */
+};
+
+typedef struct {
+  int32_t n_q_heads;             /* query heads; a multiple of n_kv_heads */
+  int32_t n_kv_heads;            /* KV heads; n_q/n_kv (the group G) in 1..16 */
+  int32_t head_dim;              /* 64 or 128 */
+  int32_t dtype;                 /* GKV_F32 or GKV_BF16: q, K, V and out */
+  int32_t n_layers;              /* number of bindable layers, >= 1 */
+  int64_t hot_capacity_tokens;   /* C_hot >= 0 */
+  int64_t cold_capacity_tokens;  /* C_cold >= 0, < 2^31 */
+  int32_t m_sat;                 /* dense threshold on M_eff; <= 0 = library default */
+  int32_t force_backend;         /* GKV_BACKEND_*; AUTO for the per-step rule */
+} gkv_config;
+
+typedef struct {
+  int64_t hot_free_tokens;     /* sum of free HOT extents */
+  int64_t hot_largest_hole;    /* longest free HOT extent */
+  int32_t hot_live_prefixes;   /* live HOT slabs */
+  int32_t hot_free_extents;    /* number of free HOT extents */
+  int64_t cold_free_slots;     /* free COLD slots */
+} gkv_stats;
+
+typedef struct gkv_ctx gkv_ctx;
+
+/* Library default for m_sat, measured on MI355X (see the dispatcher fit). */
+int32_t gkv_default_m_sat(void);
+
+/* Create a context.  Validates the config (GKV_ERR_INVALID otherwise; *out is
+ * set to NULL).  Makes no HIP call: pool bookkeeping works without a GPU. */
+int gkv_create(const gkv_config* cfg, gkv_ctx** out);
+void gkv_destroy(gkv_ctx* ctx);
+/* Last error message of this context ("" if none).  Valid until the next call. */
+const char* gkv_last_error(const gkv_ctx* ctx);
+
+/* Pools of one layer, all dev, contiguous, element type cfg.dtype:
+ *   k_hot, v_hot   [n_kv][C_hot][head_dim]   head-major: one (head, prefix)
+ *                                            slab is one linear run
+ *   k_cold, v_cold [C_cold][n_kv][head_dim]  token-major: one slot holds one
+ *                                            token of every KV head
+ * Prefix ids, HOT offsets and COLD slots are shared by all layers.  NULL is
+ * allowed for a pool whose capacity is 0. */
+int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot,
+                   void* k_cold, void* v_cold);
+
+/* Workspace bytes needed by gkv_attn_decode for steps of at most max_batch
+ * requests and at most max_suffix_tokens slot-table entries in total. */
+int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix_tokens,
+                       size_t* bytes);
+/* Bind caller-owned device workspace (dev, >= 256-byte aligned).  Also pins a
+ * small host staging ring on first use by a device call. */
+int gkv_bind_workspace(gkv_ctx* ctx, void* dev, size_t bytes);
+
+/* HOT pool (paperlayer.ai §3, reading card "Key ideas", Appendix B.8/B.10).
+ * First fit over address-ordered free extents; the slab is carved from the
+ * start of the lowest-address extent of length >= n_tokens.  Returns the new
+ * prefix id (smallest unused non-negative integer) and the slab's token
+ * offset.  GKV_ERR_NOSPACE when no single free extent fits - also when the
+ * total free space would - with no change to the pool and no demotion of
+ * live slabs; the caller then places the prefix in COLD. */
+int gkv_hot_pool_alloc(gkv_ctx* ctx, int32_t n_tokens, int32_t* prefix_id,
+                       int64_t* token_offset);
+/* Return a slab; it merges with free neighbours.  GKV_ERR_NOTFOUND for an
+ * unknown or already-freed id. */
+int gkv_hot_pool_free(gkv_ctx* ctx, int32_t prefix_id);
+/* Offset and length of a live slab (GKV_ERR_NOTFOUND otherwise). */
+int gkv_hot_prefix_info(const gkv_ctx* ctx, int32_t prefix_id, int64_t* token_offset,
+                        int32_t* n_tokens);
+
+/* COLD pool (paperlayer.ai §3: page size one token; reading card: token-level
+ * free list).  LIFO free list: a fresh pool hands out 0, 1, 2, ...; alloc pops
+ * n slots into slots_out (host, n entries) in pop order, all or nothing
+ * (GKV_ERR_NOSPACE when fewer than n are free, nothing changed). */
+int gkv_cold_pool_alloc(gkv_ctx* ctx, int32_t n, int32_t* slots_out);
+/* Push slots (host) back in the order given; the last one becomes the next
+ * handed out.  GKV_ERR_NOTFOUND, with nothing changed, if any slot is out of
+ * range, not allocated, or repeated in the call. */
+int gkv_cold_pool_free(gkv_ctx* ctx, const int32_t* slots, int32_t n);
+
+int gkv_pool_stats(const gkv_ctx* ctx, gkv_stats* out);
+
+/* Append decoded tokens into COLD (paperlayer.ai §1 "Design": COLD holds
+ * suffix and decoded tokens).  k_new, v_new: dev [n][n_kv][head_dim];
+ * slots_dev: dev int32 [n].  Row slots[i] of layer `layer`'s k_cold/v_cold
+ * becomes a byte copy of row i; other rows are untouched.  Slots outside
+ * [0, C_cold) are skipped on the device (the host cannot read them); repeated
+ * slots in one call leave one of the rows, unspecified which.  Asynchronous
+ * on `stream`. */
+int gkv_cold_append(gkv_ctx* ctx, int32_t layer, const void* k_new, const void* v_new,
+                    const int32_t* slots_dev, int32_t n, void* stream);
+
+/* One decode step of one layer (paperlayer.ai §2 "Prefix-suffix attention",
+ * §3 "Dual attention backends", §3 "Per-step dispatch").
+ *   q              dev  [B][n_q][head_dim], cfg.dtype
+ *   hot_prefix_ids host [B]: live prefix id whose HOT slab starts request b's
+ *                  context, or -1 for none (paged fallback: the whole
+ *                  context is in the slot table)
+ *   cold_indptr_h  host [B+1], cold_indptr_d dev [B+1]: the same CSR row
+ *                  pointers (non-decreasing); request b's slot table is
+ *                  cold_indices_d[indptr[b] .. indptr[b+1])
+ *   cold_indices_d dev int32: COLD slots in context order (the current token
+ *                  last).  Slots outside [0, C_cold) are clamped on the device.
+ *   out            dev  [B][n_q][head_dim], cfg.dtype
+ *   lse            dev  float [B][n_q]: natural log of the softmax
+ *                  denominator over the whole context (scores scaled by
+ *                  1/sqrt(head_dim))
+ *   backend_out    host, nullable: the prefix backend used this step
+ * Context of request b = its HOT slab's tokens, then its slot-table tokens.
+ * Query head h attends KV head h / (n_q / n_kv).  GKV_ERR_INVALID (nothing
+ * enqueued, nothing written) if B < 1, a request has neither a prefix nor a
+ * suffix, an id is not live, indptr decreases, the layer is not bound, the
+ * workspace is missing or too small, or cfg.force_backend/override is DENSE
+ * with dtype F32.  Asynchronous on `stream`. */
+int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
+                    const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
+                    const int32_t* cold_indptr_d, const int32_t* cold_indices_d,
+                    void* out, float* lse, void* stream, int32_t* backend_out);
+
+/* Per-step rule alone (host, no GPU): backend for a batch of `batch` requests
+ * under the context's threshold and override (paperlayer.ai §3 "Per-step
+ * dispatch": dense iff M_eff = B * n_q/n_kv >= M_sat). */
+int gkv_select_backend(const gkv_ctx* ctx, int32_t batch, int32_t* backend);
+/* Change the backend override (GKV_BACKEND_*) and/or threshold (> 0) of a
+ * context; m_sat <= 0 keeps the current threshold. */
+int gkv_set_dispatch(gkv_ctx* ctx, int32_t force_backend, int32_t m_sat);
+
+/* What the last successful gkv_attn_decode of this context planned (host
+ * diagnostics: no GPU needed to read it). */
+typedef struct {
+  int32_t backend;            /* GKV_BACKEND_CASCADE or GKV_BACKEND_DENSE */
+  int32_t m_eff;              /* B * n_q / n_kv of the step */
+  int32_t n_classes;          /* distinct HOT prefixes in the step */
+  int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
+  int32_t n_suffix_waves;     /* suffix work items (one wave each) */
+  int32_t n_suffix_parts;     /* slot-table chunks (partials per query head) */
+  int32_t suffix_chunk;       /* tokens per slot-table chunk */
+  int32_t pad_;
+  int64_t workspace_bytes;    /* workspace bytes the step used */
+  double host_plan_us;        /* host time spent validating and planning */
+} gkv_plan_info;
+int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GKV_H */

@@ -1,0 +1,252 @@
+"""ctypes binding of libgkv (include/gkv.h): argument marshalling only.
+
+Each method has the name of the C entry point without its ``gkv_`` prefix.
+Device buffers are passed as torch tensors (their data pointers) or as raw
+integer addresses; streams default to torch's current stream.  Every step of
+the decode path runs in the library's HIP kernels; there is no fallback: if
+libgkv.so is missing, loading raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgkv.so")
+
+GKV_OK, GKV_ERR_INVALID, GKV_ERR_NOSPACE, GKV_ERR_NOTFOUND, GKV_ERR_DEVICE = 0, -1, -2, -3, -4
+GKV_F32, GKV_BF16 = 0, 1
+BACKEND_AUTO, BACKEND_CASCADE, BACKEND_DENSE = 0, 1, 2
+BACKEND_NAMES = {BACKEND_AUTO: "auto", BACKEND_CASCADE: "cascade", BACKEND_DENSE: "dense"}
+
+
+class GkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gkv error {code}: {msg}")
+        self.code = code
+
+
+class NoSpace(GkvError):
+    pass
+
+
+class NotFound(GkvError):
+    pass
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("hot_capacity_tokens", ctypes.c_int64),
+                ("cold_capacity_tokens", ctypes.c_int64), ("m_sat", ctypes.c_int32),
+                ("force_backend", ctypes.c_int32)]
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("hot_free_tokens", ctypes.c_int64), ("hot_largest_hole", ctypes.c_int64),
+                ("hot_live_prefixes", ctypes.c_int32), ("hot_free_extents", ctypes.c_int32),
+                ("cold_free_slots", ctypes.c_int64)]
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("backend", ctypes.c_int32), ("m_eff", ctypes.c_int32),
+                ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
+                ("n_suffix_waves", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
+                ("suffix_chunk", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); the exported symbols of include/gkv.h
+SIGNATURES = {
+    "gkv_default_m_sat": (_I32, []),
+    "gkv_create": (ctypes.c_int, [ctypes.POINTER(_Config), ctypes.POINTER(_P)]),
+    "gkv_destroy": (None, [_P]),
+    "gkv_last_error": (ctypes.c_char_p, [_P]),
+    "gkv_bind_layer": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
+    "gkv_workspace_size": (ctypes.c_int, [_P, _I32, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "gkv_bind_workspace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
+    "gkv_hot_pool_alloc": (ctypes.c_int, [_P, _I32, _PI32, ctypes.POINTER(_I64)]),
+    "gkv_hot_pool_free": (ctypes.c_int, [_P, _I32]),
+    "gkv_hot_prefix_info": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I64), _PI32]),
+    "gkv_cold_pool_alloc": (ctypes.c_int, [_P, _I32, _PI32]),
+    "gkv_cold_pool_free": (ctypes.c_int, [_P, _PI32, _I32]),
+    "gkv_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(_Stats)]),
+    "gkv_cold_append": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
+    "gkv_attn_decode": (ctypes.c_int, [_P, _I32, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P, _P]),
+    "gkv_select_backend": (ctypes.c_int, [_P, _I32, _PI32]),
+    "gkv_set_dispatch": (ctypes.c_int, [_P, _I32, _I32]),
+    "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgkv.so (built by ``python -m shared_prefix_paged_contiguous_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m shared_prefix_paged_contiguous_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+class Context:
+    """One gkv_ctx: pools bookkeeping, layer bindings, workspace, dispatcher."""
+
+    def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: str,
+                 hot_capacity_tokens: int, cold_capacity_tokens: int, n_layers: int = 1,
+                 m_sat: int = 0, force_backend: int = BACKEND_AUTO):
+        self._lib = load_library()
+        self.dtype = dtype
+        cfg = _Config(n_q_heads, n_kv_heads, head_dim, GKV_BF16 if dtype == "bf16" else GKV_F32,
+                      n_layers, hot_capacity_tokens, cold_capacity_tokens, m_sat, force_backend)
+        h = _P()
+        rc = self._lib.gkv_create(ctypes.byref(cfg), ctypes.byref(h))
+        if rc != GKV_OK:
+            raise GkvError(rc, "gkv_create rejected the configuration")
+        self._h = h
+        self.cfg = cfg
+
+    # ------------------------------------------------------------ lifecycle
+    def destroy(self):
+        if getattr(self, "_h", None):
+            self._lib.gkv_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def _check(self, rc: int, what: str):
+        if rc == GKV_OK:
+            return
+        msg = f"{what}: {self._lib.gkv_last_error(self._h).decode()}"
+        if rc == GKV_ERR_NOSPACE:
+            raise NoSpace(rc, msg)
+        if rc == GKV_ERR_NOTFOUND:
+            raise NotFound(rc, msg)
+        raise GkvError(rc, msg)
+
+    # ---------------------------------------------------------------- pools
+    def hot_pool_alloc(self, n_tokens: int):
+        pid, off = ctypes.c_int32(), ctypes.c_int64()
+        self._check(self._lib.gkv_hot_pool_alloc(self._h, n_tokens, ctypes.byref(pid), ctypes.byref(off)),
+                    "hot_pool_alloc")
+        return pid.value, off.value
+
+    def hot_pool_free(self, prefix_id: int):
+        self._check(self._lib.gkv_hot_pool_free(self._h, prefix_id), "hot_pool_free")
+
+    def hot_prefix_info(self, prefix_id: int):
+        off, n = ctypes.c_int64(), ctypes.c_int32()
+        self._check(self._lib.gkv_hot_prefix_info(self._h, prefix_id, ctypes.byref(off), ctypes.byref(n)),
+                    "hot_prefix_info")
+        return off.value, n.value
+
+    def cold_pool_alloc(self, n: int) -> np.ndarray:
+        out = np.empty(max(n, 0), dtype=np.int32)
+        self._check(self._lib.gkv_cold_pool_alloc(self._h, n, out.ctypes.data_as(_PI32)), "cold_pool_alloc")
+        return out
+
+    def cold_pool_free(self, slots):
+        s = _i32(slots)
+        self._check(self._lib.gkv_cold_pool_free(self._h, s.ctypes.data_as(_PI32), len(s)), "cold_pool_free")
+
+    def pool_stats(self) -> dict:
+        st = _Stats()
+        self._check(self._lib.gkv_pool_stats(self._h, ctypes.byref(st)), "pool_stats")
+        return {f: getattr(st, f) for f, _ in _Stats._fields_}
+
+    # --------------------------------------------------------------- memory
+    def bind_layer(self, layer: int, k_hot, v_hot, k_cold, v_cold):
+        self._check(self._lib.gkv_bind_layer(self._h, layer, _ptr(k_hot), _ptr(v_hot), _ptr(k_cold),
+                                             _ptr(v_cold)), "bind_layer")
+
+    def workspace_size(self, max_batch: int, max_suffix_tokens: int) -> int:
+        b = ctypes.c_size_t()
+        self._check(self._lib.gkv_workspace_size(self._h, max_batch, max_suffix_tokens, ctypes.byref(b)),
+                    "workspace_size")
+        return b.value
+
+    def bind_workspace(self, dev, nbytes: Optional[int] = None):
+        if nbytes is None:
+            nbytes = dev.numel() * dev.element_size()
+        self._check(self._lib.gkv_bind_workspace(self._h, _ptr(dev), nbytes), "bind_workspace")
+
+    # ------------------------------------------------------------- device ops
+    def cold_append(self, layer: int, k_new, v_new, slots_dev, n: Optional[int] = None, stream=None):
+        if n is None:
+            n = slots_dev.numel()
+        self._check(self._lib.gkv_cold_append(self._h, layer, _ptr(k_new), _ptr(v_new), _ptr(slots_dev), n,
+                                              _stream(stream)), "cold_append")
+
+    def attn_decode(self, layer: int, q, hot_prefix_ids, cold_indptr_h, cold_indptr_d, cold_indices_d,
+                    out, lse, batch: Optional[int] = None, stream=None) -> int:
+        ids = _i32(hot_prefix_ids)
+        ind = _i32(cold_indptr_h)
+        if batch is None:
+            batch = len(ids)
+        backend = ctypes.c_int32()
+        self._check(self._lib.gkv_attn_decode(
+            self._h, layer, _ptr(q), batch, ids.ctypes.data_as(_PI32), ind.ctypes.data_as(_PI32),
+            _ptr(cold_indptr_d), _ptr(cold_indices_d), _ptr(out), _ptr(lse), _stream(stream),
+            ctypes.byref(backend)), "attn_decode")
+        return backend.value
+
+    # ------------------------------------------------------------ dispatcher
+    def select_backend(self, batch: int) -> int:
+        b = ctypes.c_int32()
+        self._check(self._lib.gkv_select_backend(self._h, batch, ctypes.byref(b)), "select_backend")
+        return b.value
+
+    def set_dispatch(self, force_backend: int = BACKEND_AUTO, m_sat: int = 0):
+        self._check(self._lib.gkv_set_dispatch(self._h, force_backend, m_sat), "set_dispatch")
+
+    def last_plan(self) -> dict:
+        p = _PlanInfo()
+        self._check(self._lib.gkv_last_plan(self._h, ctypes.byref(p)), "last_plan")
+        return {f: getattr(p, f) for f, _ in _PlanInfo._fields_ if f != "pad_"}
+
+
+def default_m_sat() -> int:
+    return load_library().gkv_default_m_sat()

@@ -1,0 +1,383 @@
+// C ABI of libgkv (declared in include/gkv.h).  Host code: validation, pool
+// bookkeeping, the per-step planner and the staging of work lists; every
+// step of the attention itself runs in the kernels of kernels.hip.
+
+#include <hip/hip_runtime.h>
+
+#include <chrono>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/gkv.h"
+#include "kernels.h"
+#include "plan.h"
+#include "pools.h"
+
+namespace {
+
+// M_sat on MI355X: the smallest M_eff from which the dense prefix kernel is
+// never slower than the cascade one, from the dispatcher fit over the
+// Qwen-2.5-14B and Llama-3.1-8B head shapes at L_p = 16K.
+constexpr int32_t kDefaultMSat = 1024;
+constexpr int kRing = 4;   // pinned staging buffers in flight
+
+struct Layer {
+  void* k_hot = nullptr;
+  void* v_hot = nullptr;
+  void* k_cold = nullptr;
+  void* v_cold = nullptr;
+  bool bound = false;
+};
+
+struct Stage {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct gkv_ctx {
+  gkv_config cfg;
+  gkv::HotPool hot;
+  gkv::ColdPool cold;
+  std::vector<Layer> layers;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t m_sat;
+  int32_t force;
+  std::string err;
+  Stage ring[kRing];
+  int ring_pos = 0;
+  std::vector<uint8_t> blob;
+  std::vector<int32_t> scratch_ids;
+  gkv_plan_info last{};
+  bool have_last = false;
+
+  explicit gkv_ctx(const gkv_config& c)
+      : cfg(c),
+        hot(c.hot_capacity_tokens),
+        cold(static_cast<int32_t>(c.cold_capacity_tokens)),
+        layers(c.n_layers),
+        m_sat(c.m_sat > 0 ? c.m_sat : kDefaultMSat),
+        force(c.force_backend) {}
+};
+
+namespace {
+
+int fail(gkv_ctx* ctx, int code, const std::string& msg) {
+  if (ctx) ctx->err = msg;
+  return code;
+}
+
+int device_fail(gkv_ctx* ctx, const char* what, hipError_t e) {
+  return fail(ctx, GKV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t elem_size(const gkv_config& c) { return c.dtype == GKV_BF16 ? 2 : 4; }
+
+gkv::PlanShape shape_of(const gkv_config& c) {
+  return gkv::PlanShape{c.n_q_heads, c.n_kv_heads, c.head_dim};
+}
+
+int check_layer(gkv_ctx* ctx, int32_t layer) {
+  if (layer < 0 || layer >= ctx->cfg.n_layers)
+    return fail(ctx, GKV_ERR_INVALID, "layer " + std::to_string(layer) + " out of range");
+  if (!ctx->layers[layer].bound)
+    return fail(ctx, GKV_ERR_INVALID, "layer " + std::to_string(layer) + " is not bound");
+  return GKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gkv_default_m_sat(void) { return kDefaultMSat; }
+
+int gkv_create(const gkv_config* cfg, gkv_ctx** out) {
+  if (!out) return GKV_ERR_INVALID;
+  *out = nullptr;
+  if (!cfg) return GKV_ERR_INVALID;
+  const gkv_config& c = *cfg;
+  if (c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.n_q_heads % c.n_kv_heads != 0) return GKV_ERR_INVALID;
+  const int32_t group = c.n_q_heads / c.n_kv_heads;
+  if (group > 16) return GKV_ERR_INVALID;
+  if (c.head_dim != 64 && c.head_dim != 128) return GKV_ERR_INVALID;
+  if (c.dtype != GKV_F32 && c.dtype != GKV_BF16) return GKV_ERR_INVALID;
+  if (c.n_layers < 1) return GKV_ERR_INVALID;
+  if (c.hot_capacity_tokens < 0 || c.cold_capacity_tokens < 0 ||
+      c.cold_capacity_tokens > 0x7fffffffLL || c.hot_capacity_tokens > (1LL << 40))
+    return GKV_ERR_INVALID;
+  if (c.force_backend < GKV_BACKEND_AUTO || c.force_backend > GKV_BACKEND_DENSE) return GKV_ERR_INVALID;
+  if (c.force_backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) return GKV_ERR_INVALID;
+  gkv_ctx* ctx = new (std::nothrow) gkv_ctx(c);
+  if (!ctx) return GKV_ERR_INVALID;
+  *out = ctx;
+  return GKV_OK;
+}
+
+void gkv_destroy(gkv_ctx* ctx) {
+  if (!ctx) return;
+  for (Stage& s : ctx->ring) {
+    if (s.ev) {
+      hipEventSynchronize(s.ev);
+      hipEventDestroy(s.ev);
+    }
+    if (s.host) hipHostFree(s.host);
+  }
+  delete ctx;
+}
+
+const char* gkv_last_error(const gkv_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot, void* k_cold, void* v_cold) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (layer < 0 || layer >= ctx->cfg.n_layers)
+    return fail(ctx, GKV_ERR_INVALID, "layer " + std::to_string(layer) + " out of range");
+  if (ctx->cfg.hot_capacity_tokens > 0 && (!k_hot || !v_hot))
+    return fail(ctx, GKV_ERR_INVALID, "HOT pool pointers are NULL");
+  if (ctx->cfg.cold_capacity_tokens > 0 && (!k_cold || !v_cold))
+    return fail(ctx, GKV_ERR_INVALID, "COLD pool pointers are NULL");
+  for (void* p : {k_hot, v_hot, k_cold, v_cold})
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+      return fail(ctx, GKV_ERR_INVALID, "pool pointers must be 16-byte aligned");
+  ctx->layers[layer] = Layer{k_hot, v_hot, k_cold, v_cold, true};
+  return GKV_OK;
+}
+
+int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix_tokens, size_t* bytes) {
+  if (!ctx || !bytes || max_batch < 1 || max_suffix_tokens < 0) return GKV_ERR_INVALID;
+  const gkv::PlanShape s = shape_of(ctx->cfg);
+  const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * 4;
+  const int64_t pr = gkv::prefix_rows_bound(s, max_batch);
+  const int64_t sr = gkv::suffix_rows_bound(s, max_batch, max_suffix_tokens);
+  *bytes = gkv::align256(gkv::plan_blob_bound(s, max_batch, max_suffix_tokens)) +
+           gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
+           gkv::align256(sr * 4);
+  return GKV_OK;
+}
+
+int gkv_bind_workspace(gkv_ctx* ctx, void* dev, size_t bytes) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (!dev || reinterpret_cast<uintptr_t>(dev) % 256 != 0)
+    return fail(ctx, GKV_ERR_INVALID, "workspace must be a non-null 256-byte aligned device pointer");
+  ctx->ws = dev;
+  ctx->ws_bytes = bytes;
+  return GKV_OK;
+}
+
+int gkv_hot_pool_alloc(gkv_ctx* ctx, int32_t n_tokens, int32_t* prefix_id, int64_t* token_offset) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (!prefix_id || !token_offset || n_tokens <= 0)
+    return fail(ctx, GKV_ERR_INVALID, "hot_pool_alloc: n_tokens must be >= 1 and outputs non-null");
+  const int r = ctx->hot.alloc(n_tokens, prefix_id, token_offset);
+  if (r == -2)
+    return fail(ctx, GKV_ERR_NOSPACE, "no free HOT extent of " + std::to_string(n_tokens) + " tokens");
+  return GKV_OK;
+}
+
+int gkv_hot_pool_free(gkv_ctx* ctx, int32_t prefix_id) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (ctx->hot.release(prefix_id) != 0)
+    return fail(ctx, GKV_ERR_NOTFOUND, "prefix id " + std::to_string(prefix_id) + " is not live");
+  return GKV_OK;
+}
+
+int gkv_hot_prefix_info(const gkv_ctx* ctx, int32_t prefix_id, int64_t* token_offset, int32_t* n_tokens) {
+  if (!ctx || !token_offset || !n_tokens) return GKV_ERR_INVALID;
+  return ctx->hot.lookup(prefix_id, token_offset, n_tokens) ? GKV_OK : GKV_ERR_NOTFOUND;
+}
+
+int gkv_cold_pool_alloc(gkv_ctx* ctx, int32_t n, int32_t* slots_out) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (n < 0 || (n > 0 && !slots_out)) return fail(ctx, GKV_ERR_INVALID, "cold_pool_alloc: bad arguments");
+  if (ctx->cold.alloc(n, slots_out) != 0)
+    return fail(ctx, GKV_ERR_NOSPACE, std::to_string(n) + " COLD slots requested, " +
+                                          std::to_string(ctx->cold.free_count()) + " free");
+  return GKV_OK;
+}
+
+int gkv_cold_pool_free(gkv_ctx* ctx, const int32_t* slots, int32_t n) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (n < 0 || (n > 0 && !slots)) return fail(ctx, GKV_ERR_INVALID, "cold_pool_free: bad arguments");
+  if (ctx->cold.release(slots, n) != 0)
+    return fail(ctx, GKV_ERR_NOTFOUND, "cold_pool_free: a slot is out of range, not allocated or repeated");
+  return GKV_OK;
+}
+
+int gkv_pool_stats(const gkv_ctx* ctx, gkv_stats* out) {
+  if (!ctx || !out) return GKV_ERR_INVALID;
+  out->hot_free_tokens = ctx->hot.free_tokens();
+  out->hot_largest_hole = ctx->hot.largest_hole();
+  out->hot_live_prefixes = ctx->hot.live_count();
+  out->hot_free_extents = ctx->hot.extent_count();
+  out->cold_free_slots = ctx->cold.free_count();
+  return GKV_OK;
+}
+
+int gkv_cold_append(gkv_ctx* ctx, int32_t layer, const void* k_new, const void* v_new,
+                    const int32_t* slots_dev, int32_t n, void* stream) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (int r = check_layer(ctx, layer)) return r;
+  if (n < 0) return fail(ctx, GKV_ERR_INVALID, "cold_append: n < 0");
+  if (n == 0) return GKV_OK;
+  if (!k_new || !v_new || !slots_dev) return fail(ctx, GKV_ERR_INVALID, "cold_append: null pointer");
+  if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+    return fail(ctx, GKV_ERR_INVALID, "cold_append: rows must be 16-byte aligned");
+  if (ctx->cfg.cold_capacity_tokens == 0) return fail(ctx, GKV_ERR_INVALID, "COLD pool is empty");
+  const Layer& L = ctx->layers[layer];
+  const int64_t row_bytes =
+      static_cast<int64_t>(ctx->cfg.n_kv_heads) * ctx->cfg.head_dim * static_cast<int64_t>(elem_size(ctx->cfg));
+  hipError_t e = gkv::launch_cold_append(k_new, v_new, slots_dev, n, L.k_cold, L.v_cold, row_bytes,
+                                         static_cast<int32_t>(ctx->cfg.cold_capacity_tokens),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, "cold_append launch", e);
+  return GKV_OK;
+}
+
+int gkv_select_backend(const gkv_ctx* ctx, int32_t batch, int32_t* backend) {
+  if (!ctx || !backend || batch < 1) return GKV_ERR_INVALID;
+  int32_t b = gkv::choose_backend(batch, ctx->cfg.n_q_heads / ctx->cfg.n_kv_heads, ctx->m_sat, ctx->force);
+  if (b == GKV_BACKEND_DENSE && ctx->cfg.dtype != GKV_BF16) b = GKV_BACKEND_CASCADE;
+  *backend = b;
+  return GKV_OK;
+}
+
+int gkv_set_dispatch(gkv_ctx* ctx, int32_t force_backend, int32_t m_sat) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (force_backend < GKV_BACKEND_AUTO || force_backend > GKV_BACKEND_DENSE)
+    return fail(ctx, GKV_ERR_INVALID, "unknown backend");
+  if (force_backend == GKV_BACKEND_DENSE && ctx->cfg.dtype != GKV_BF16)
+    return fail(ctx, GKV_ERR_INVALID, "the dense backend is bf16 only");
+  ctx->force = force_backend;
+  if (m_sat > 0) ctx->m_sat = m_sat;
+  return GKV_OK;
+}
+
+int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out) {
+  if (!ctx || !out) return GKV_ERR_INVALID;
+  if (!ctx->have_last) return GKV_ERR_NOTFOUND;
+  *out = ctx->last;
+  return GKV_OK;
+}
+
+int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
+                    const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
+                    const int32_t* cold_indptr_d, const int32_t* cold_indices_d, void* out,
+                    float* lse, void* stream, int32_t* backend_out) {
+  if (!ctx) return GKV_ERR_INVALID;
+  const auto t_start = std::chrono::steady_clock::now();
+  if (int r = check_layer(ctx, layer)) return r;
+  if (batch < 1) return fail(ctx, GKV_ERR_INVALID, "batch must be >= 1");
+  if (!q || !out || !lse || !hot_prefix_ids || !cold_indptr_h)
+    return fail(ctx, GKV_ERR_INVALID, "attn_decode: null pointer argument");
+  if (!ctx->ws) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
+  const gkv_config& c = ctx->cfg;
+  const int32_t group = c.n_q_heads / c.n_kv_heads;
+  const bool any_suffix = cold_indptr_h[batch] != cold_indptr_h[0];
+  if (any_suffix && (!cold_indptr_d || !cold_indices_d))
+    return fail(ctx, GKV_ERR_INVALID, "attn_decode: slot table pointers are null");
+  if (any_suffix && c.cold_capacity_tokens == 0)
+    return fail(ctx, GKV_ERR_INVALID, "slot tables given but the COLD pool is empty");
+
+  int32_t backend = gkv::choose_backend(batch, group, ctx->m_sat, ctx->force);
+  if (backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) {
+    if (ctx->force == GKV_BACKEND_DENSE) return fail(ctx, GKV_ERR_INVALID, "the dense backend is bf16 only");
+    backend = GKV_BACKEND_CASCADE;
+  }
+
+  gkv::Plan plan;
+  std::string err;
+  if (gkv::build_plan(shape_of(c), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, ctx->blob, plan,
+                      err) != 0)
+    return fail(ctx, GKV_ERR_INVALID, err);
+
+  // workspace: [plan blob][prefix o][prefix lse][suffix o][suffix lse]
+  const size_t row = static_cast<size_t>(c.head_dim) * 4;
+  const size_t off_po = gkv::align256(plan.blob_bytes);
+  const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
+  const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
+  const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
+  const size_t need = off_sl + gkv::align256(plan.suffix_rows * 4);
+  if (need > ctx->ws_bytes)
+    return fail(ctx, GKV_ERR_INVALID, "workspace too small: step needs " + std::to_string(need) +
+                                          " bytes, " + std::to_string(ctx->ws_bytes) + " bound");
+
+  // stage the plan through a pinned buffer of the ring
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Stage& sg = ctx->ring[ctx->ring_pos];
+  ctx->ring_pos = (ctx->ring_pos + 1) % kRing;
+  hipError_t e;
+  if (sg.pending) {
+    if ((e = hipEventSynchronize(sg.ev)) != hipSuccess) return device_fail(ctx, "staging event wait", e);
+    sg.pending = false;
+  }
+  if (!sg.ev && (e = hipEventCreateWithFlags(&sg.ev, hipEventDisableTiming)) != hipSuccess)
+    return device_fail(ctx, "hipEventCreate", e);
+  if (sg.cap < plan.blob_bytes) {
+    if (sg.host) hipHostFree(sg.host);
+    sg.host = nullptr;
+    sg.cap = 0;
+    const size_t cap = gkv::align256(plan.blob_bytes * 2);
+    if ((e = hipHostMalloc(&sg.host, cap, hipHostMallocDefault)) != hipSuccess)
+      return device_fail(ctx, "hipHostMalloc(staging)", e);
+    sg.cap = cap;
+  }
+  std::memcpy(sg.host, ctx->blob.data(), plan.blob_bytes);
+  const auto t_planned = std::chrono::steady_clock::now();
+  if ((e = hipMemcpyAsync(ctx->ws, sg.host, plan.blob_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
+    return device_fail(ctx, "work-list copy", e);
+  if ((e = hipEventRecord(sg.ev, st)) != hipSuccess) return device_fail(ctx, "hipEventRecord", e);
+  sg.pending = true;
+
+  const Layer& L = ctx->layers[layer];
+  uint8_t* ws = static_cast<uint8_t*>(ctx->ws);
+  gkv::StepArgs a{};
+  a.batch = batch;
+  a.n_q = c.n_q_heads;
+  a.n_kv = c.n_kv_heads;
+  a.group = group;
+  a.head_dim = c.head_dim;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(c.head_dim)));
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.k_hot = L.k_hot;
+  a.v_hot = L.v_hot;
+  a.hot_cap = c.hot_capacity_tokens;
+  a.k_cold = L.k_cold;
+  a.v_cold = L.v_cold;
+  a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
+  a.cold_indices = cold_indices_d;
+  a.classes = reinterpret_cast<const gkv::PrefixClass*>(ws + plan.off_classes);
+  a.members = reinterpret_cast<const int32_t*>(ws + plan.off_members);
+  a.prefix_items = reinterpret_cast<const gkv::PrefixItem*>(ws + plan.off_prefix);
+  a.n_prefix_items = plan.n_classes > 0 ? plan.n_prefix_items : 0;
+  a.suffix_items = reinterpret_cast<const gkv::SuffixItem*>(ws + plan.off_suffix);
+  a.n_suffix_items = plan.n_suffix_items;
+  a.reqs = reinterpret_cast<const gkv::ReqInfo*>(ws + plan.off_reqs);
+  a.p_o = reinterpret_cast<float*>(ws + off_po);
+  a.p_lse = reinterpret_cast<float*>(ws + off_pl);
+  a.s_o = reinterpret_cast<float*>(ws + off_so);
+  a.s_lse = reinterpret_cast<float*>(ws + off_sl);
+  if ((e = gkv::launch_step(a, c.dtype, backend, st)) != hipSuccess) return device_fail(ctx, "step launch", e);
+
+  ctx->last.backend = backend;
+  ctx->last.m_eff = plan.m_eff;
+  ctx->last.n_classes = plan.n_classes;
+  ctx->last.n_prefix_blocks = a.n_prefix_items;
+  ctx->last.n_suffix_waves = plan.n_suffix_items;
+  ctx->last.n_suffix_parts = plan.n_chunks;
+  ctx->last.suffix_chunk = plan.suffix_chunk;
+  ctx->last.workspace_bytes = static_cast<int64_t>(need);
+  ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
+  ctx->have_last = true;
+  if (backend_out) *backend_out = backend;
+  return GKV_OK;
+}
+
+}  // extern "C"

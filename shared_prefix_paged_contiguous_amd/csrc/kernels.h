@@ -1,0 +1,22 @@
+// Launchers of the device kernels (implemented in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan_types.h"
+
+namespace gkv {
+
+// Byte copy of n token rows (row_bytes each, a multiple of 16) into the COLD
+// pool rows named by slots (dev); slots outside [0, cold_cap) are skipped.
+hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_t* slots,
+                              int32_t n, void* k_cold, void* v_cold, int64_t row_bytes,
+                              int32_t cold_cap, hipStream_t stream);
+
+// Prefix kernel of the chosen backend (when there are prefix items), the
+// suffix kernel (when there are suffix items), then the merge.
+hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream);
+
+}  // namespace gkv

@@ -1,0 +1,114 @@
+#include "pools.h"
+
+#include <algorithm>
+
+namespace gkv {
+
+HotPool::HotPool(int64_t capacity) : capacity_(capacity) {
+  if (capacity_ > 0) free_.emplace(0, capacity_);
+}
+
+int HotPool::alloc(int32_t n, int32_t* id, int64_t* offset) {
+  for (auto it = free_.begin(); it != free_.end(); ++it) {   // lowest address first
+    if (it->second < n) continue;
+    const int64_t off = it->first;
+    const int64_t rest = it->second - n;
+    free_.erase(it);
+    if (rest > 0) free_.emplace(off + n, rest);
+    int32_t pid;
+    if (!released_ids_.empty()) {
+      pid = *released_ids_.begin();
+      released_ids_.erase(released_ids_.begin());
+    } else {
+      pid = next_id_++;
+    }
+    live_.emplace(pid, Slab{off, n});
+    *id = pid;
+    *offset = off;
+    return 0;
+  }
+  return -2;
+}
+
+int HotPool::release(int32_t id) {
+  auto it = live_.find(id);
+  if (it == live_.end()) return -3;
+  int64_t off = it->second.offset;
+  int64_t len = it->second.len;
+  live_.erase(it);
+  released_ids_.insert(id);
+  // merge with the free extent that ends where this one starts
+  auto next = free_.lower_bound(off);
+  if (next != free_.begin()) {
+    auto prev = std::prev(next);
+    if (prev->first + prev->second == off) {
+      off = prev->first;
+      len += prev->second;
+      free_.erase(prev);
+    }
+  }
+  // ... and with the one that starts where it ends
+  next = free_.find(off + len);
+  if (next != free_.end()) {
+    len += next->second;
+    free_.erase(next);
+  }
+  free_.emplace(off, len);
+  return 0;
+}
+
+bool HotPool::lookup(int32_t id, int64_t* offset, int32_t* len) const {
+  auto it = live_.find(id);
+  if (it == live_.end()) return false;
+  *offset = it->second.offset;
+  *len = it->second.len;
+  return true;
+}
+
+int64_t HotPool::free_tokens() const {
+  int64_t t = 0;
+  for (const auto& e : free_) t += e.second;
+  return t;
+}
+
+int64_t HotPool::largest_hole() const {
+  int64_t m = 0;
+  for (const auto& e : free_) m = std::max(m, e.second);
+  return m;
+}
+
+ColdPool::ColdPool(int32_t capacity)
+    : capacity_(capacity), allocated_(capacity, 0), mark_(capacity, 0) {
+  stack_.reserve(capacity);
+  for (int32_t s = capacity - 1; s >= 0; --s) stack_.push_back(s);
+}
+
+int ColdPool::alloc(int32_t n, int32_t* out) {
+  if (static_cast<int64_t>(n) > static_cast<int64_t>(stack_.size())) return -2;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = stack_.back();
+    stack_.pop_back();
+    allocated_[s] = 1;
+    out[i] = s;
+  }
+  return 0;
+}
+
+int ColdPool::release(const int32_t* slots, int32_t n) {
+  if (++stamp_ == 0) {   // stamp wrapped: clear the marks once
+    std::fill(mark_.begin(), mark_.end(), 0u);
+    stamp_ = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = slots[i];
+    if (s < 0 || s >= capacity_ || !allocated_[s] || mark_[s] == stamp_) return -3;
+    mark_[s] = stamp_;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    allocated_[slots[i]] = 0;
+    stack_.push_back(slots[i]);
+  }
+  return 0;
+}
+
+}  // namespace gkv

@@ -1,0 +1,119 @@
+"""Device-side set-up of a synthetic decode step (used by tests and bench.py).
+
+Given a ``workloads.Workload`` it creates a library context, replays the
+workload's placement through the context's own allocators (HOT first, COLD
+fallback for prefixes that do not fit, permuted COLD free order for the
+suffix slots), writes the prefix slabs into the HOT pool with torch (the
+caller's prefill, outside the decode path), appends every suffix token into
+the COLD pool with ``cold_append``, and builds the per-request CSR slot table.
+"""
+
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import binding, workloads
+
+
+class DecodeState:
+    def __init__(self, w: workloads.Workload, device: str = "cuda", n_layers: int = 1,
+                 m_sat: int = 0, force_backend: int = binding.BACKEND_AUTO,
+                 hot_capacity: Optional[int] = None, cold_capacity: Optional[int] = None):
+        s = w.spec
+        self.w = w
+        self.device = device
+        self.dtype = w.torch_dtype
+        self.hot_cap = s.hot_capacity if hot_capacity is None else hot_capacity
+        self.cold_cap = s.cold_capacity if cold_capacity is None else cold_capacity
+        self.n_layers = n_layers
+        self.ctx = binding.Context(s.n_q, s.n_kv, s.head_dim, s.dtype, self.hot_cap, self.cold_cap,
+                                   n_layers=n_layers, m_sat=m_sat, force_backend=force_backend)
+        ctx = self.ctx
+
+        def hot_alloc(n):
+            try:
+                return ctx.hot_pool_alloc(n)
+            except binding.NoSpace:
+                return None
+
+        self.placement = workloads.place(w, hot_alloc, ctx.hot_pool_free, ctx.cold_pool_alloc,
+                                         ctx.cold_pool_free)
+        pl = self.placement
+
+        n_kv, d = s.n_kv, s.head_dim
+        dev = torch.device(device)
+        k_hot = torch.zeros((n_kv, max(self.hot_cap, 1), d), dtype=self.dtype, device=dev)
+        v_hot = torch.zeros_like(k_hot)
+        k_cold = torch.zeros((max(self.cold_cap, 1), n_kv, d), dtype=self.dtype, device=dev)
+        v_cold = torch.zeros_like(k_cold)
+        for p, ln in enumerate(w.prefix_lens):
+            off = pl["prefix_offset"][p]
+            if off >= 0:
+                k_hot[:, off:off + ln, :] = w.prefix_k[p].to(dev).permute(1, 0, 2)
+                v_hot[:, off:off + ln, :] = w.prefix_v[p].to(dev).permute(1, 0, 2)
+        self.pools = [(k_hot, v_hot, k_cold, v_cold)]
+        ctx.bind_layer(0, k_hot, v_hot, k_cold, v_cold)
+
+        # COLD rows: fallen-back prefixes, then every suffix token, via cold_append
+        rows_k, rows_v, slots = [], [], []
+        for p, sl in pl["prefix_slots"].items():
+            rows_k.append(w.prefix_k[p]); rows_v.append(w.prefix_v[p]); slots.append(sl)
+        rows_k.append(w.suffix_k); rows_v.append(w.suffix_v)
+        slots.append(np.concatenate([pl["req_slots"][b] for b in range(w.batch)]) if w.batch else
+                     np.zeros(0, np.int32))
+        all_slots = np.concatenate(slots).astype(np.int32)
+        if len(all_slots):
+            self.append(0, torch.cat(rows_k).to(dev), torch.cat(rows_v).to(dev),
+                        torch.from_numpy(all_slots).to(dev))
+
+        # per-request context: HOT id (or -1 and the prefix slots up front), then suffix slots
+        ids: List[int] = []
+        tables = []
+        for b in range(w.batch):
+            p = int(w.request_prefix[b])
+            t = []
+            if p >= 0 and pl["prefix_id"][p] >= 0:
+                ids.append(pl["prefix_id"][p])
+            else:
+                ids.append(-1)
+                if p >= 0:
+                    t.append(pl["prefix_slots"][p])
+            t.append(pl["req_slots"][b])
+            tables.append(np.concatenate(t))
+        self.hot_ids = np.asarray(ids, dtype=np.int32)
+        lens = np.asarray([len(t) for t in tables], dtype=np.int64)
+        indptr = np.zeros(w.batch + 1, dtype=np.int64)
+        np.cumsum(lens, out=indptr[1:])
+        assert indptr[-1] < 2 ** 31
+        self.indptr_h = indptr.astype(np.int32)
+        self.indices_h = (np.concatenate(tables) if tables else np.zeros(0)).astype(np.int32)
+        self.indptr_d = torch.from_numpy(self.indptr_h).to(dev)
+        self.indices_d = torch.from_numpy(self.indices_h).to(dev)
+        self.q = w.q.to(dev)
+        ws_bytes = ctx.workspace_size(w.batch, int(self.indptr_h[-1]))
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ctx.bind_workspace(self.workspace)
+        for layer in range(1, n_layers):
+            self.add_layer_copy(layer)
+
+    def append(self, layer, k_rows, v_rows, slots_dev):
+        self.ctx.cold_append(layer, k_rows.contiguous(), v_rows.contiguous(), slots_dev)
+
+    def add_layer_copy(self, layer: int):
+        """Bind a copy of layer 0's pools as `layer` (distinct memory, same data)."""
+        k_hot, v_hot, k_cold, v_cold = (t.clone() for t in self.pools[0])
+        self.pools.append((k_hot, v_hot, k_cold, v_cold))
+        self.ctx.bind_layer(layer, k_hot, v_hot, k_cold, v_cold)
+
+    def new_outputs(self):
+        s = self.w.spec
+        out = torch.empty((self.w.batch, s.n_q, s.head_dim), dtype=self.dtype, device=self.device)
+        lse = torch.empty((self.w.batch, s.n_q), dtype=torch.float32, device=self.device)
+        return out, lse
+
+    def run(self, out, lse, layer: int = 0, stream=None) -> int:
+        return self.ctx.attn_decode(layer, self.q, self.hot_ids, self.indptr_h, self.indptr_d,
+                                    self.indices_d, out, lse, stream=stream)

@@ -158,7 +158,7 @@ def make(name_or_spec, *, seed: Optional[int] = None, dtype: Optional[str] = Non
         class_sizes = rng.integers(spec.class_lo, spec.class_hi + 1, size=spec.n_prefixes)
         request_prefix = np.repeat(np.arange(spec.n_prefixes), class_sizes)
         request_prefix = request_prefix[rng.permutation(len(request_prefix))].astype(np.int32)
-        hot_churn = rng.integers(512, 2048 + 1, size=4).tolist()
+        hot_churn = rng.integers(4096, 16384 + 1, size=4).tolist()
         n_b = len(request_prefix)
     else:
         n_b = spec.batch

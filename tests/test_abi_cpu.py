@@ -1,0 +1,234 @@
+"""CPU tests of libgkv: the shared library loads, exports every symbol the
+header declares, and its host-side logic (pool bookkeeping, dispatcher rule,
+argument checks) matches the oracle's models bit for bit.  No device call is
+made: these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import oracle
+from oracle.alloc import ColdAllocModel, HotAllocModel
+from shared_prefix_paged_contiguous_amd import binding, workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    try:
+        return binding.load_library()
+    except ImportError as e:
+        pytest.skip(str(e))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "gkv.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[a-z_0-9]+\s*\*?\s+)+\*?\s*(gkv_[a-z_0-9]+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_binding_signatures():
+    names = declared_symbols()
+    assert len(names) >= 18
+    assert set(names) == set(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib_or_skip()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def _ctx(**kw):
+    _lib_or_skip()
+    args = dict(n_q_heads=8, n_kv_heads=2, head_dim=64, dtype="f32", hot_capacity_tokens=100,
+                cold_capacity_tokens=6)
+    args.update(kw)
+    return binding.Context(**args)
+
+
+def test_create_rejects_bad_configs():
+    _lib_or_skip()
+    for kw in [dict(n_q_heads=10, n_kv_heads=4), dict(head_dim=96), dict(n_q_heads=34, n_kv_heads=2),
+               dict(hot_capacity_tokens=-1), dict(cold_capacity_tokens=2 ** 31),
+               dict(dtype="f32", force_backend=binding.BACKEND_DENSE)]:
+        with pytest.raises(binding.GkvError):
+            _ctx(**kw)
+
+
+def test_hot_pool_matches_hand_trace_and_model():
+    c = _ctx()
+    m = HotAllocModel(100)
+    seq = [("a", 30), ("a", 20), ("a", 40), ("f", 1), ("a", 25), ("a", 15), ("a", 10), ("f", 0),
+           ("f", 2), ("a", 31), ("f", 1), ("f", 1), ("f", 3)]
+    for op, x in seq:
+        if op == "a":
+            try:
+                want = m.alloc(x)
+            except oracle.NoSpace:
+                with pytest.raises(binding.NoSpace):
+                    c.hot_pool_alloc(x)
+                continue
+            assert c.hot_pool_alloc(x) == want
+            assert c.hot_prefix_info(want[0]) == (want[1], x)
+        else:
+            try:
+                m.free(x)
+            except oracle.NotFound:
+                with pytest.raises(binding.NotFound):
+                    c.hot_pool_free(x)
+                continue
+            c.hot_pool_free(x)
+        s = c.pool_stats()
+        assert s["hot_free_tokens"] == m.free_tokens()
+        assert s["hot_largest_hole"] == m.largest_hole()
+        assert s["hot_free_extents"] == len(m.free_extents)
+        assert s["hot_live_prefixes"] == len(m.live)
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.tuples(st.sampled_from(["a", "f"]), st.integers(1, 50)), max_size=80))
+def test_hot_pool_bit_exact_vs_model(seq):
+    c = _ctx(hot_capacity_tokens=160)
+    m = HotAllocModel(160)
+    for op, x in seq:
+        if op == "a":
+            try:
+                want = m.alloc(x)
+            except oracle.NoSpace:
+                with pytest.raises(binding.NoSpace):
+                    c.hot_pool_alloc(x)
+                continue
+            assert c.hot_pool_alloc(x) == want
+        else:
+            pid = sorted(m.live)[x % len(m.live)] if m.live else x
+            if pid in m.live:
+                m.free(pid)
+                c.hot_pool_free(pid)
+            else:
+                with pytest.raises(binding.NotFound):
+                    c.hot_pool_free(pid)
+    s = c.pool_stats()
+    assert (s["hot_free_tokens"], s["hot_largest_hole"]) == (m.free_tokens(), m.largest_hole())
+
+
+def test_cold_pool_matches_hand_trace():
+    c = _ctx(cold_capacity_tokens=6)
+    assert c.cold_pool_alloc(3).tolist() == [0, 1, 2]
+    c.cold_pool_free([2, 0])
+    assert c.cold_pool_alloc(2).tolist() == [0, 2]
+    assert c.cold_pool_alloc(2).tolist() == [3, 4]
+    with pytest.raises(binding.NoSpace):
+        c.cold_pool_alloc(2)
+    for bad in ([1, 5], [1, 1], [7], [-1]):
+        with pytest.raises(binding.NotFound):
+            c.cold_pool_free(bad)
+    assert c.pool_stats()["cold_free_slots"] == 1
+    c.cold_pool_free([4, 1, 3])
+    assert c.cold_pool_alloc(4).tolist() == [3, 1, 4, 5]
+    assert c.cold_pool_alloc(0).tolist() == []
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.lists(st.tuples(st.sampled_from(["a", "f"]), st.integers(0, 9)), max_size=80))
+def test_cold_pool_bit_exact_vs_model(seq):
+    c = _ctx(cold_capacity_tokens=30)
+    m = ColdAllocModel(30)
+    live = []
+    for op, x in seq:
+        if op == "a":
+            try:
+                want = m.alloc(x)
+            except oracle.NoSpace:
+                with pytest.raises(binding.NoSpace):
+                    c.cold_pool_alloc(x)
+                continue
+            assert c.cold_pool_alloc(x).tolist() == want
+            live += want
+        else:
+            k = min(x, len(live))
+            out, live = live[-k:][::-1] if k else [], live[:-k] if k else live
+            m.free(out)
+            c.cold_pool_free(out)
+    assert c.pool_stats()["cold_free_slots"] == m.free_count()
+
+
+@pytest.mark.parametrize("name", ["tiny", "hetero8"])
+def test_workload_placement_bit_exact_vs_models(name):
+    """The slot maps and HOT offsets the C allocators give for a workload's
+    placement equal the oracle models' (the GPU tests read these slots)."""
+    _lib_or_skip()
+    w = workloads.make(name)
+    s = w.spec
+    c = binding.Context(s.n_q, s.n_kv, s.head_dim, s.dtype, s.hot_capacity, s.cold_capacity)
+
+    def c_hot(n):
+        try:
+            return c.hot_pool_alloc(n)
+        except binding.NoSpace:
+            return None
+
+    hm, cm = HotAllocModel(s.hot_capacity), ColdAllocModel(s.cold_capacity)
+
+    def m_hot(n):
+        try:
+            return hm.alloc(n)
+        except oracle.NoSpace:
+            return None
+
+    a = workloads.place(w, c_hot, c.hot_pool_free, c.cold_pool_alloc, c.cold_pool_free)
+    b = workloads.place(w, m_hot, hm.free, cm.alloc, cm.free)
+    assert a["prefix_id"] == b["prefix_id"] and a["prefix_offset"] == b["prefix_offset"]
+    for x, y in zip(a["req_slots"], b["req_slots"]):
+        assert np.array_equal(x, np.asarray(y, dtype=np.int32))
+    if name == "hetero8":
+        # churn left holes: some slab landed below the running sum of lengths
+        assert min(o for o in a["prefix_offset"] if o >= 0) < sum(w.hot_churn[:1])
+
+
+def test_dispatch_rule_matches_model_and_pages():
+    c = _ctx(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", m_sat=1024)
+    for bsz in [1, 8, 32, 128, 255, 256, 257, 512]:
+        assert c.select_backend(bsz) == oracle.choose_backend(bsz, 32, 8, 1024)
+    c.set_dispatch(binding.BACKEND_CASCADE)
+    assert c.select_backend(512) == binding.BACKEND_CASCADE
+    c.set_dispatch(binding.BACKEND_AUTO, 64)
+    assert c.select_backend(16) == binding.BACKEND_DENSE
+    assert c.select_backend(15) == binding.BACKEND_CASCADE
+    f = _ctx(m_sat=1)   # fp32: the dense kernel is bf16 only, AUTO stays on cascade
+    assert f.select_backend(64) == binding.BACKEND_CASCADE
+    with pytest.raises(binding.GkvError):
+        f.set_dispatch(binding.BACKEND_DENSE)
+    assert binding.default_m_sat() > 0
+
+
+def test_attn_decode_rejects_bad_steps_before_any_device_work():
+    c = _ctx()
+    pid, _ = c.hot_pool_alloc(10)
+    # nothing bound yet
+    with pytest.raises(binding.GkvError, match="not bound"):
+        c.attn_decode(0, 16, [pid], [0, 0], 0, 0, 16, 16, stream=0)
+    c.bind_layer(0, 16, 16, 16, 16)   # fake aligned addresses: only host checks run below
+    with pytest.raises(binding.GkvError, match="workspace"):
+        c.attn_decode(0, 16, [pid], [0, 0], 0, 0, 16, 16, stream=0)
+    c.bind_workspace(256, 1 << 20)
+    cases = [([-1], [0, 0], "neither"), ([pid + 7], [0, 1], "not live"), ([pid, pid], [0, 2, 1], "decreases"),
+             ([-2], [0, 1], "< -1")]
+    for ids, indptr, msg in cases:
+        with pytest.raises(binding.GkvError, match=msg):
+            c.attn_decode(0, 16, ids, indptr, 16, 16, 16, 16, batch=len(ids), stream=0)
+    with pytest.raises(binding.GkvError, match="too small"):
+        c2 = _ctx()
+        c2.bind_layer(0, 16, 16, 16, 16)
+        c2.bind_workspace(256, 256)
+        c2.attn_decode(0, 16, [-1], [0, 3], 16, 16, 16, 16, stream=0)
+
+
+def test_workspace_bound_covers_plans():
+    c = _ctx(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", hot_capacity_tokens=16384,
+             cold_capacity_tokens=65536)
+    assert c.workspace_size(64, 65536) > c.workspace_size(4, 100) > 0

@@ -1,0 +1,228 @@
+"""GPU parity of libgkv against the float64 oracle, through the C ABI.
+
+Every case draws a seeded synthetic workload, places it with the library's
+own allocators, appends the suffix tokens with gkv_cold_append, runs
+gkv_attn_decode on the GPU and compares out / lse with the oracle's softmax
+attention over the logical context (prefix || suffix) element by element.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.append import append_model
+from shared_prefix_paged_contiguous_amd import binding, workloads
+from shared_prefix_paged_contiguous_amd.harness import DecodeState
+from tests.gpu_helpers import check, f64, oracle_ref
+
+pytestmark = pytest.mark.gpu
+
+CASCADE, DENSE, AUTO = binding.BACKEND_CASCADE, binding.BACKEND_DENSE, binding.BACKEND_AUTO
+FP32_TOL = dict(atol=1e-4, rtol=1e-4, norm_rel=1e-4, lse_abs=1e-4)
+
+
+def run(w, force=AUTO, **kw):
+    st = DecodeState(w, force_backend=force, **kw)
+    out, lse = st.new_outputs()
+    backend = st.run(out, lse)
+    torch.cuda.synchronize()
+    return st, out, lse, backend
+
+
+def spec(**kw):
+    base = dict(name="case", n_q=32, n_kv=8, head_dim=128, dtype="bf16", batch=8, prefix_len=1000,
+                suffix_lo=0, suffix_hi=0, hot_capacity=1200, cold_capacity=8192)
+    base.update(kw)
+    return workloads.Spec(**base)
+
+
+# --------------------------------------------------------------- cold append
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cold_append_bit_exact(dtype):
+    torch.manual_seed(0)
+    n_kv, d, cap = 2, 64, 300
+    ctx = binding.Context(8, n_kv, d, dtype, 0, cap)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    k_cold = torch.randn(cap, n_kv, d).to(td).cuda()
+    v_cold = torch.randn(cap, n_kv, d).to(td).cuda()
+    before_k, before_v = k_cold.cpu().clone(), v_cold.cpu().clone()
+    ctx.bind_layer(0, None, None, k_cold, v_cold)
+    slots = ctx.cold_pool_alloc(40)[np.random.default_rng(1).permutation(40)]
+    slots_ext = np.concatenate([slots, [cap, -5]]).astype(np.int32)   # out of range: skipped
+    k_new = torch.randn(len(slots_ext), n_kv, d).to(td)
+    v_new = torch.randn(len(slots_ext), n_kv, d).to(td)
+    ctx.cold_append(0, k_new.cuda(), v_new.cuda(), torch.from_numpy(slots_ext).cuda())
+    torch.cuda.synchronize()
+    want_k = append_model(before_k.view(torch.int16 if dtype == "bf16" else torch.int32).numpy(), slots,
+                          k_new[:40].view(torch.int16 if dtype == "bf16" else torch.int32).numpy())
+    want_v = append_model(before_v.view(torch.int16 if dtype == "bf16" else torch.int32).numpy(), slots,
+                          v_new[:40].view(torch.int16 if dtype == "bf16" else torch.int32).numpy())
+    got_k = k_cold.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy()
+    got_v = v_cold.cpu().view(torch.int16 if dtype == "bf16" else torch.int32).numpy()
+    assert got_k.tobytes() == want_k.tobytes()
+    assert got_v.tobytes() == want_v.tobytes()
+
+
+# ------------------------------------------------------------- tiny configs
+def test_tiny_fp32_parity():
+    w = workloads.make("tiny")
+    st, out, lse, backend = run(w)
+    assert backend == CASCADE        # M_eff = 16 < M_sat, and fp32 has no dense kernel
+    ref_o, ref_l = oracle_ref(w)
+    check(out, lse, ref_o, ref_l, **FP32_TOL)
+
+
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_tiny_bf16_parity(force):
+    w = workloads.make("tiny", dtype="bf16")
+    st, out, lse, backend = run(w, force=force)
+    assert backend == force
+    check(out, lse, *oracle_ref(w))
+
+
+# --------------------------------------------------- several tiles, ragged
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_ragged_multi_tile_parity(force):
+    # prefix 1000 = 15 full 64-token tiles + 40; suffixes cover empty, single
+    # token, tile-1, tile, tile+1, several chunks
+    s = spec(batch=8, fixed_suffix=(0, 1, 31, 32, 33, 257, 700, 1500))
+    w = workloads.make(s)
+    st, out, lse, backend = run(w, force=force)
+    assert backend == force
+    check(out, lse, *oracle_ref(w))
+
+
+@pytest.mark.parametrize("n_q,n_kv,d", [(8, 8, 128), (16, 1, 128), (10, 2, 128), (32, 8, 64), (20, 4, 64)])
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_group_and_head_dim_parity(n_q, n_kv, d, force):
+    s = spec(n_q=n_q, n_kv=n_kv, head_dim=d, batch=5, prefix_len=333, hot_capacity=400,
+             fixed_suffix=(5, 64, 0, 100, 190))
+    w = workloads.make(s)
+    _, out, lse, _ = run(w, force=force)
+    check(out, lse, *oracle_ref(w))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp32_head_dims(d):
+    s = spec(dtype="f32", head_dim=d, batch=3, prefix_len=200, hot_capacity=256, fixed_suffix=(0, 77, 300))
+    w = workloads.make(s)
+    _, out, lse, _ = run(w)
+    check(out, lse, *oracle_ref(w), **FP32_TOL)
+
+
+def test_single_request_single_token():
+    s = spec(batch=1, prefix_len=0, hot_capacity=0, fixed_suffix=(1,))
+    w = workloads.make(s)
+    _, out, lse, _ = run(w)
+    ref_o, ref_l = oracle_ref(w)
+    check(out, lse, ref_o, ref_l)
+    # one token: the output is that token's V row (exactly, up to bf16 output rounding)
+    v = f64(w.suffix_v[0])
+    g = np.arange(32) // 4
+    assert np.abs(f64(out)[0] - v[g]).max() <= 2 ** -8 * np.abs(v).max()
+
+
+# ------------------------------------------------ paged fallback & classes
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_cold_fallback_equals_hot(force):
+    """The same logical step with the prefix in HOT and, with a HOT pool too
+    small for it, in COLD at the front of every slot table (the admission
+    fallback): both match the oracle, and the HOT run's output is unchanged
+    by the slot placement."""
+    s = spec(batch=6, prefix_len=900, fixed_suffix=(3, 50, 0, 129, 64, 400))
+    w = workloads.make(s)
+    _, out_hot, lse_hot, _ = run(w, force=force)
+    st, out_cold, lse_cold, _ = run(w, force=force, hot_capacity=512)   # 900 does not fit
+    assert all(i == -1 for i in st.hot_ids)
+    ref = oracle_ref(w)
+    check(out_hot, lse_hot, *ref)
+    check(out_cold, lse_cold, *ref)
+
+
+def test_mixed_prefix_and_suffix_only_requests():
+    s = spec(batch=6, prefix_len=700, fixed_suffix=(10, 0, 40, 1, 300, 64))
+    w = workloads.make(s)
+    w.request_prefix[[2, 4]] = -1     # two requests without a HOT prefix
+    _, out, lse, _ = run(w)
+    check(out, lse, *oracle_ref(w))
+
+
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_heterogeneous_classes(force):
+    s = dataclasses.replace(workloads.SPECS["hetero8"], n_prefixes=3, prefix_len_lo=100, prefix_len_hi=1100,
+                            class_lo=1, class_hi=4, suffix_lo=0, suffix_hi=300, hot_capacity=4096,
+                            cold_capacity=8192)
+    w = workloads.make(s)
+    st, out, lse, _ = run(w, force=force)
+    assert st.ctx.last_plan()["n_classes"] == len(set(w.request_prefix.tolist()))
+    check(out, lse, *oracle_ref(w))
+
+
+def test_placement_invariance_is_bitwise():
+    """Moving the slab and permuting the COLD slots changes no output bit:
+    the kernels sum in an order set by the logical sequence alone."""
+    s = spec(batch=4, prefix_len=600, hot_capacity=2000, fixed_suffix=(100, 33, 0, 500))
+    w1 = workloads.make(s)
+    _, o1, l1, _ = run(w1)
+    w2 = dataclasses.replace(w1, cold_perm=np.random.default_rng(5).permutation(s.cold_capacity).astype(np.int32),
+                             hot_churn=[300, 500])   # hole [0,300) too small: slab moves to 800
+    st2, o2, l2, _ = run(w2)
+    assert st2.placement["prefix_offset"][0] == 800
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeated_calls_identical_and_failed_call_writes_nothing():
+    w = workloads.make(spec(batch=3, fixed_suffix=(10, 20, 30)))
+    st = DecodeState(w)
+    out, lse = st.new_outputs()
+    st.run(out, lse)
+    out2, lse2 = st.new_outputs()
+    st.run(out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    sentinel = torch.full_like(out, 7.0)
+    with pytest.raises(binding.GkvError):
+        st.ctx.attn_decode(0, st.q, [st.hot_ids[0] + 9] * 3, st.indptr_h, st.indptr_d, st.indices_d,
+                           sentinel, lse)
+    torch.cuda.synchronize()
+    assert bool((sentinel == 7.0).all())
+
+
+def test_dispatch_follows_m_eff():
+    s = spec(batch=16, n_q=32, n_kv=8, fixed_suffix=tuple([8] * 16))
+    w = workloads.make(s)
+    st = DecodeState(w, m_sat=64)              # M_eff = 16 * 4 = 64 >= 64: dense
+    out, lse = st.new_outputs()
+    assert st.run(out, lse) == DENSE
+    st.ctx.set_dispatch(AUTO, 65)              # 64 < 65: cascade
+    assert st.run(out, lse) == CASCADE
+    torch.cuda.synchronize()
+    check(out, lse, *oracle_ref(w))
+
+
+# ------------------------------------------------- full-size configurations
+FULL = ["llama8b_lp16k_b64", "qwen14b_tp2_lp16k_b128", "hetero8", "qwen32b_tp4_lp1k_b256"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_requests(name):
+    """The workloads at their full sizes, in the launch configuration the
+    benchmark times (AUTO dispatch), checked on sampled requests (the oracle
+    computes each one from scratch), plus the other backend forced."""
+    w = workloads.make(name)
+    rng = np.random.default_rng(11)
+    req = sorted(set(rng.choice(w.batch, size=4, replace=False).tolist() + [0, w.batch - 1]))
+    ref_o, ref_l = oracle_ref(w, requests=req)
+    st = DecodeState(w)
+    out, lse = st.new_outputs()
+    b = st.run(out, lse)
+    torch.cuda.synchronize()
+    check(out, lse, ref_o, ref_l, requests=req)
+    other = DENSE if b == CASCADE else CASCADE
+    st.ctx.set_dispatch(other)
+    out2, lse2 = st.new_outputs()
+    st.run(out2, lse2)
+    torch.cuda.synchronize()
+    check(out2, lse2, ref_o, ref_l, requests=req)
