@@ -1,0 +1,306 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of shared-prefix attention on one MI355X.
+
+A step is the whole hot path for one layer: gkv_cold_append of the batch's
+new tokens into the COLD pool, then gkv_attn_decode (host dispatch, prefix
+kernel of the chosen backend, COLD suffix gather kernel, log-sum-exp merge).
+Default workload: Llama-3.1-8B attention shape (32 query / 8 KV heads,
+head_dim 128, bf16), one 16384-token shared prefix in HOT, 64 requests with
+suffixes of 128-1024 tokens scattered token-wise in COLD (seeded N(0,1)
+synthetic data standing in for the pages' ShareGPT-V3 workload).
+
+Consecutive steps rotate over R copies of the pools ("layers", >= 1 GiB in
+total) so that each step reads its K/V from HBM rather than from the 256 MB
+Infinity Cache.  Prints one JSON line (metric, value = query-tokens/s, ...,
+roofline of the dominant kernel, cpu_baseline of the float64 oracle).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --fit-msat        # dispatcher threshold sweep (JSON lines)
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s + achieved HBM GB/s, Llama-3.1-8B shape, L_p=16K, B=64"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+MALL_DEFEAT_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, st):
+    """Bytes and flops the method must move / do in one step, whole step and
+    per kernel.  K/V of each distinct HOT prefix count once (read once per
+    step), every suffix token once; partials and work lists are overhead and
+    do not count."""
+    s = w.spec
+    e = 2 if s.dtype == "bf16" else 4
+    d, n_kv, n_q, bsz = s.head_dim, s.n_kv, s.n_q, w.batch
+    ids = st.hot_ids
+    classes = sorted(set(int(i) for i in ids if i >= 0))
+    pre_tokens = sum(st.ctx.hot_prefix_info(c)[1] for c in classes)
+    tab = np.diff(st.indptr_h.astype(np.int64))
+    suf_tokens = int(tab.sum())
+    n_pre_req, n_suf_req = int((ids >= 0).sum()), int((tab > 0).sum())
+    q_row = n_q * d * e
+    kv_row = n_kv * d * e
+    k = {"prefix": 2 * pre_tokens * kv_row + n_pre_req * q_row,
+         "suffix": 2 * suf_tokens * kv_row + 4 * suf_tokens + n_suf_req * q_row,
+         "merge": bsz * q_row + 4 * bsz * n_q}
+    append = 2 * 2 * n_suf_req * kv_row + 4 * n_suf_req
+    step = (2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + 4 * (bsz + 1)
+            + bsz * q_row + bsz * q_row + 4 * bsz * n_q + append)
+    group = n_q // n_kv
+    flops_prefix = sum(4 * int((ids == c).sum()) * group * st.ctx.hot_prefix_info(c)[1] * d * n_kv
+                       for c in classes)
+    return {"kernel_bytes": k, "append_bytes": append, "step_bytes": step,
+            "prefix_flops": flops_prefix, "suffix_flops": 4 * n_q * d * suf_tokens,
+            "prefix_tokens": pre_tokens, "suffix_tokens": suf_tokens}
+
+
+def estimate_step_bytes(w):
+    s = w.spec
+    e = 2 if s.dtype == "bf16" else 4
+    used = sorted(set(int(p) for p in w.request_prefix if p >= 0))
+    tokens = sum(w.prefix_lens[p] for p in used) + int(w.suffix_lens.sum())
+    return 2 * tokens * s.n_kv * s.head_dim * e
+
+
+def cpu_baseline(w, target_s: float):
+    """The float64 oracle, unmodified, on a bounded sample of requests."""
+    import torch
+    import threadpoolctl
+
+    from oracle.attention import decode_step
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+
+    pk = [f64(x) for x in w.prefix_k]
+    pv = [f64(x) for x in w.prefix_v]
+    q = f64(w.q)
+    done, t_used = [], 0.0
+    t_all = time.perf_counter()
+    for b in range(w.batch):
+        sk, sv = w.suffix_rows(b)
+        sks = [None] * w.batch
+        svs = [None] * w.batch
+        sks[b], svs[b] = f64(sk), f64(sv)
+        t = time.perf_counter()
+        decode_step(q, pk, pv, w.request_prefix, sks, svs, requests=[b])
+        t_used += time.perf_counter() - t
+        done.append(b)
+        if time.perf_counter() - t_all >= target_s:
+            break
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": len(done) / t_used, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} of {w.batch} requests of the same workload (all {w.spec.n_q} query "
+                      f"heads each), float64 numpy; BLAS threads={threads}, host cpus={os.cpu_count()}; "
+                      f"{t_used:.1f} s of oracle time"}
+
+
+def build_state(w, replicas, force):
+    from shared_prefix_paged_contiguous_amd.harness import DecodeState
+    return DecodeState(w, n_layers=replicas, force_backend=force)
+
+
+def step_inputs(w, st):
+    """The batch's current tokens: the last slot-table entry of each request
+    and its K/V row (appending them again rewrites identical bytes)."""
+    import torch
+    tab = np.diff(st.indptr_h.astype(np.int64))
+    reqs = np.nonzero(tab > 0)[0]
+    slots = st.indices_h[st.indptr_h[1:][reqs] - 1]
+    last = w.suffix_offsets[1:][reqs] - 1
+    k_new = w.suffix_k[torch.from_numpy(last)].to(st.device).contiguous()
+    v_new = w.suffix_v[torch.from_numpy(last)].to(st.device).contiguous()
+    return k_new, v_new, torch.from_numpy(slots.astype(np.int32)).to(st.device)
+
+
+def run_bench(args):
+    import torch
+
+    from shared_prefix_paged_contiguous_amd import binding, workloads
+
+    t_setup = time.perf_counter()
+    w = workloads.make(args.workload)
+    s = w.spec
+    force = {"auto": binding.BACKEND_AUTO, "cascade": binding.BACKEND_CASCADE,
+             "dense": binding.BACKEND_DENSE}[args.backend]
+    replicas = args.replicas or max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
+    st = build_state(w, replicas, force)
+    alg = algorithmic(w, st)
+    k_new, v_new, slots_new = step_inputs(w, st)
+    out, lse = st.new_outputs()
+    ctx = st.ctx
+    stream = torch.cuda.current_stream()
+    log(f"[bench] workload={s.name} B={w.batch} replicas={replicas} step_bytes={alg['step_bytes']/1e6:.1f} MB "
+        f"setup={time.perf_counter()-t_setup:.1f}s")
+
+    def step(i):
+        layer = i % replicas
+        ctx.cold_append(layer, k_new, v_new, slots_new, stream=stream)
+        return st.run(out, lse, layer=layer, stream=stream)
+
+    backend = None
+    for i in range(args.warmup):
+        backend = step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        backend = step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    plan = ctx.last_plan()
+    log(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step (wall {wall*1e3/args.steps:.1f} us/step), "
+        f"backend={binding.BACKEND_NAMES[backend]}, host plan {plan['host_plan_us']:.2f} us")
+
+    # same-layer ("warm", cache-resident) timing, reported for contrast only
+    e0.record(stream)
+    for i in range(args.steps):
+        ctx.cold_append(0, k_new, v_new, slots_new, stream=stream)
+        st.run(out, lse, layer=0, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_warm = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations with HIP events recorded by the library on this stream
+    ctx.kernel_timing(args.steps)
+    for i in range(args.steps):
+        step(i)
+    per = ctx.kernel_timing_read(args.steps)
+    ctx.kernel_timing(0)
+    kern_ms = {"prefix": float(per[:, 0].mean()), "suffix": float(per[:, 1].mean()),
+               "merge": float(per[:, 2].mean())}
+    log(f"[bench] kernel avg us: " + ", ".join(f"{k}={v*1e3:.1f}" for k, v in kern_ms.items()))
+
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_bytes = alg["kernel_bytes"][dom]
+    achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom + "_kernel",
+                "kernel_us": round(kern_ms[dom] * 1e3, 2), "kernel_bytes": dom_bytes}
+    if kern_ms["prefix"] > 0 and alg["prefix_flops"] > 0:
+        roofline["prefix_mfma_frac"] = round(alg["prefix_flops"] / (kern_ms["prefix"] * 1e-3) / 1e12
+                                             / BF16_PEAK_TFLOPS, 4)
+    value = w.batch / (ms_step * 1e-3)
+    step_gbps = alg["step_bytes"] / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
+        "data": "synthetic (seeded N(0,1), bf16-rounded; stands in for ShareGPT-V3)",
+        "config": {"workload": s.name, "description": s.description, "batch": w.batch,
+                   "n_q_heads": s.n_q, "n_kv_heads": s.n_kv, "head_dim": s.head_dim,
+                   "prefix_tokens": alg["prefix_tokens"], "suffix_tokens": alg["suffix_tokens"],
+                   "backend": binding.BACKEND_NAMES[backend], "m_eff": plan["m_eff"],
+                   "replicas": replicas},
+        "achieved_hbm_gbps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+        "step_bytes": alg["step_bytes"],
+        "warm_ms_per_step": round(ms_warm, 5),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
+        "host_plan_us": round(plan["host_plan_us"], 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on a bounded sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def fit_msat(args):
+    """Time both prefix kernels (prefix-only steps) over a batch sweep and
+    report the smallest M_eff from which dense is never slower."""
+    import torch
+
+    from shared_prefix_paged_contiguous_amd import binding, workloads
+    from shared_prefix_paged_contiguous_amd.harness import DecodeState
+
+    rows = []
+    for name in args.fit_workloads.split(","):
+        g = workloads.SPECS[name].n_q // workloads.SPECS[name].n_kv
+        for bsz in [int(x) for x in args.fit_batches.split(",")]:
+            w = workloads.make(name, batch=bsz, suffix_range=(1, 1))
+            st = DecodeState(w, n_layers=2)
+            out, lse = st.new_outputs()
+            res = {"workload": name, "batch": bsz, "m_eff": bsz * g}
+            for label, force in (("cascade", binding.BACKEND_CASCADE), ("dense", binding.BACKEND_DENSE)):
+                st.ctx.set_dispatch(force)
+                for i in range(5):
+                    st.run(out, lse, layer=i % 2)
+                st.ctx.kernel_timing(20)
+                for i in range(20):
+                    st.run(out, lse, layer=i % 2)
+                per = st.ctx.kernel_timing_read(20)
+                st.ctx.kernel_timing(0)
+                res[label + "_prefix_us"] = round(float(per[:, 0].mean()) * 1e3, 2)
+                flops = 4 * bsz * g * w.prefix_lens[0] * w.spec.head_dim * w.spec.n_kv
+                res[label + "_mfma_frac"] = round(flops / (per[:, 0].mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+            rows.append(res)
+            print(json.dumps(res), flush=True)
+            del st
+            torch.cuda.empty_cache()
+    for name in args.fit_workloads.split(","):
+        pts = sorted((r for r in rows if r["workload"] == name), key=lambda r: r["m_eff"])
+        m_sat = None
+        for i, r in enumerate(pts):
+            if all(p["dense_prefix_us"] <= p["cascade_prefix_us"] for p in pts[i:]):
+                m_sat = r["m_eff"]
+                break
+        print(json.dumps({"workload": name, "fitted_m_sat": m_sat}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_lp16k_b64")
+    ap.add_argument("--backend", default="auto", choices=["auto", "cascade", "dense"])
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--fit-msat", action="store_true")
+    ap.add_argument("--fit-workloads", default="qwen14b_tp2_lp16k_b128,llama8b_lp16k_b64")
+    ap.add_argument("--fit-batches", default="8,16,32,64,128,192,256,384,512")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
+              "KV head with no exchange inside attention; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.fit_msat:
+        fit_msat(args)
+        return
+    res = run_bench(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

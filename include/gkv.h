@@ -155,9 +155,11 @@ int gkv_cold_append(gkv_ctx* ctx, int32_t layer, const void* k_new, const void* 
  *   hot_prefix_ids host [B]: live prefix id whose HOT slab starts request b's
  *                  context, or -1 for none (paged fallback: the whole
  *                  context is in the slot table)
- *   cold_indptr_h  host [B+1], cold_indptr_d dev [B+1]: the same CSR row
- *                  pointers (non-decreasing); request b's slot table is
- *                  cold_indices_d[indptr[b] .. indptr[b+1])
+ *   cold_indptr_h  host [B+1]: CSR row pointers (non-decreasing); request
+ *                  b's slot table is cold_indices_d[indptr[b] .. indptr[b+1]).
+ *                  The kernels receive this host copy in their arguments.
+ *   cold_indptr_d  dev [B+1], nullable: a device copy of the same pointers,
+ *                  kept for callers that hold one; not read
  *   cold_indices_d dev int32: COLD slots in context order (the current token
  *                  last).  Slots outside [0, C_cold) are clamped on the device.
  *   out            dev  [B][n_q][head_dim], cfg.dtype
@@ -191,14 +193,26 @@ typedef struct {
   int32_t m_eff;              /* B * n_q / n_kv of the step */
   int32_t n_classes;          /* distinct HOT prefixes in the step */
   int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
-  int32_t n_suffix_waves;     /* suffix work items (one wave each) */
-  int32_t n_suffix_parts;     /* slot-table chunks (partials per query head) */
-  int32_t suffix_chunk;       /* tokens per slot-table chunk */
+  int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV heads) */
+  int32_t n_suffix_parts;     /* slot-table parts (>= one per request) */
+  int32_t merge_kernel;       /* 1 if a request spanned several parts */
   int32_t pad_;
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
 } gkv_plan_info;
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
+
+/* Per-kernel timing, for measurement.  With capacity > 0, each following
+ * gkv_attn_decode records HIP events on its stream before its first kernel
+ * and after each of its prefix, suffix and merge kernels, for up to
+ * `capacity` calls (then recording stops until read).  capacity 0 disables
+ * it and releases the events.  Creating the events is a HIP call. */
+int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity);
+/* Waits for the recorded calls and writes, per call i, the milliseconds of
+ * its prefix, suffix and merge kernels into ms[3i], ms[3i+1], ms[3i+2] (0
+ * for a kernel the call did not launch); *n = number of calls written
+ * (<= max_calls).  Clears the record. */
+int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* n);
 
 #ifdef __cplusplus
 }

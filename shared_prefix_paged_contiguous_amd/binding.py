@@ -55,8 +55,8 @@ class _Stats(ctypes.Structure):
 class _PlanInfo(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("m_eff", ctypes.c_int32),
                 ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
-                ("n_suffix_waves", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
-                ("suffix_chunk", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
+                ("merge_kernel", ctypes.c_int32), ("pad_", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
 
 
@@ -85,6 +85,8 @@ SIGNATURES = {
     "gkv_select_backend": (ctypes.c_int, [_P, _I32, _PI32]),
     "gkv_set_dispatch": (ctypes.c_int, [_P, _I32, _I32]),
     "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
+    "gkv_kernel_timing": (ctypes.c_int, [_P, _I32]),
+    "gkv_kernel_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), _I32, _PI32]),
 }
 
 _lib = None
@@ -241,6 +243,18 @@ class Context:
 
     def set_dispatch(self, force_backend: int = BACKEND_AUTO, m_sat: int = 0):
         self._check(self._lib.gkv_set_dispatch(self._h, force_backend, m_sat), "set_dispatch")
+
+    def kernel_timing(self, capacity: int):
+        self._check(self._lib.gkv_kernel_timing(self._h, capacity), "kernel_timing")
+
+    def kernel_timing_read(self, max_calls: int) -> np.ndarray:
+        """[calls, 3] milliseconds of the prefix, suffix and merge kernels."""
+        ms = np.zeros((max(max_calls, 1), 3), dtype=np.float32)
+        n = ctypes.c_int32()
+        self._check(self._lib.gkv_kernel_timing_read(
+            self._h, ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), max_calls, ctypes.byref(n)),
+            "kernel_timing_read")
+        return ms[:n.value]
 
     def last_plan(self) -> dict:
         p = _PlanInfo()

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstring>
@@ -22,7 +23,6 @@ namespace {
 // never slower than the cascade one, from the dispatcher fit over the
 // Qwen-2.5-14B and Llama-3.1-8B head shapes at L_p = 16K.
 constexpr int32_t kDefaultMSat = 1024;
-constexpr int kRing = 4;   // pinned staging buffers in flight
 
 struct Layer {
   void* k_hot = nullptr;
@@ -30,13 +30,6 @@ struct Layer {
   void* k_cold = nullptr;
   void* v_cold = nullptr;
   bool bound = false;
-};
-
-struct Stage {
-  void* host = nullptr;
-  size_t cap = 0;
-  hipEvent_t ev = nullptr;
-  bool pending = false;
 };
 
 }  // namespace
@@ -51,10 +44,11 @@ struct gkv_ctx {
   int32_t m_sat;
   int32_t force;
   std::string err;
-  Stage ring[kRing];
-  int ring_pos = 0;
-  std::vector<uint8_t> blob;
-  std::vector<int32_t> scratch_ids;
+  gkv::StepArgs args;   // kernel-argument block of the current step (~9 KB)
+  std::vector<hipEvent_t> timing_events;   // 4 per recorded call
+  int32_t timing_capacity = 0;
+  int32_t timing_used = 0;
+  std::vector<int32_t> timing_launched;    // per recorded call: bit 0 prefix, bit 1 suffix
   gkv_plan_info last{};
   bool have_last = false;
 
@@ -122,12 +116,9 @@ int gkv_create(const gkv_config* cfg, gkv_ctx** out) {
 
 void gkv_destroy(gkv_ctx* ctx) {
   if (!ctx) return;
-  for (Stage& s : ctx->ring) {
-    if (s.ev) {
-      hipEventSynchronize(s.ev);
-      hipEventDestroy(s.ev);
-    }
-    if (s.host) hipHostFree(s.host);
+  for (hipEvent_t e : ctx->timing_events) {
+    hipEventSynchronize(e);
+    hipEventDestroy(e);
   }
   delete ctx;
 }
@@ -155,9 +146,7 @@ int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix
   const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * 4;
   const int64_t pr = gkv::prefix_rows_bound(s, max_batch);
   const int64_t sr = gkv::suffix_rows_bound(s, max_batch, max_suffix_tokens);
-  *bytes = gkv::align256(gkv::plan_blob_bound(s, max_batch, max_suffix_tokens)) +
-           gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
-           gkv::align256(sr * 4);
+  *bytes = gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) + gkv::align256(sr * 4);
   return GKV_OK;
 }
 
@@ -265,6 +254,49 @@ int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out) {
   return GKV_OK;
 }
 
+int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (capacity < 0 || capacity > (1 << 20)) return fail(ctx, GKV_ERR_INVALID, "timing capacity out of range");
+  for (hipEvent_t e : ctx->timing_events) {
+    hipEventSynchronize(e);
+    hipEventDestroy(e);
+  }
+  ctx->timing_events.clear();
+  ctx->timing_capacity = 0;
+  ctx->timing_used = 0;
+  ctx->timing_launched.assign(capacity, 0);
+  for (int32_t i = 0; i < 4 * capacity; ++i) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return device_fail(ctx, "hipEventCreate(timing)", r);
+    ctx->timing_events.push_back(e);
+  }
+  ctx->timing_capacity = capacity;
+  return GKV_OK;
+}
+
+int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* n) {
+  if (!ctx || !n || max_calls < 0 || (max_calls > 0 && !ms)) return GKV_ERR_INVALID;
+  const int32_t k = std::min(ctx->timing_used, max_calls);
+  for (int32_t i = 0; i < ctx->timing_used; ++i) {
+    hipError_t r = hipEventSynchronize(ctx->timing_events[4 * i + 3]);
+    if (r != hipSuccess) return device_fail(ctx, "timing event wait", r);
+  }
+  for (int32_t i = 0; i < k; ++i) {
+    hipEvent_t* ev = &ctx->timing_events[4 * i];
+    for (int j = 0; j < 3; ++j) {
+      float t = 0.f;
+      hipError_t r = hipEventElapsedTime(&t, ev[j], ev[j + 1]);
+      if (r != hipSuccess) return device_fail(ctx, "hipEventElapsedTime", r);
+      const bool launched = j == 2 || (ctx->timing_launched[i] >> j & 1);
+      ms[3 * i + j] = launched ? t : 0.f;
+    }
+  }
+  *n = k;
+  ctx->timing_used = 0;
+  return GKV_OK;
+}
+
 int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
                     const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
                     const int32_t* cold_indptr_d, const int32_t* cold_indices_d, void* out,
@@ -279,8 +311,9 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   const gkv_config& c = ctx->cfg;
   const int32_t group = c.n_q_heads / c.n_kv_heads;
   const bool any_suffix = cold_indptr_h[batch] != cold_indptr_h[0];
-  if (any_suffix && (!cold_indptr_d || !cold_indices_d))
-    return fail(ctx, GKV_ERR_INVALID, "attn_decode: slot table pointers are null");
+  if (any_suffix && !cold_indices_d)
+    return fail(ctx, GKV_ERR_INVALID, "attn_decode: slot table pointer is null");
+  (void)cold_indptr_d;
   if (any_suffix && c.cold_capacity_tokens == 0)
     return fail(ctx, GKV_ERR_INVALID, "slot tables given but the COLD pool is empty");
 
@@ -292,51 +325,23 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
 
   gkv::Plan plan;
   std::string err;
-  if (gkv::build_plan(shape_of(c), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, ctx->blob, plan,
-                      err) != 0)
+  gkv::StepArgs& a = ctx->args;
+  if (gkv::build_plan(shape_of(c), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
     return fail(ctx, GKV_ERR_INVALID, err);
 
-  // workspace: [plan blob][prefix o][prefix lse][suffix o][suffix lse]
+  // workspace: [prefix o][prefix lse][suffix o][suffix lse]
   const size_t row = static_cast<size_t>(c.head_dim) * 4;
-  const size_t off_po = gkv::align256(plan.blob_bytes);
-  const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
+  const size_t off_pl = gkv::align256(plan.prefix_rows * row);
   const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
   const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
   const size_t need = off_sl + gkv::align256(plan.suffix_rows * 4);
   if (need > ctx->ws_bytes)
     return fail(ctx, GKV_ERR_INVALID, "workspace too small: step needs " + std::to_string(need) +
                                           " bytes, " + std::to_string(ctx->ws_bytes) + " bound");
-
-  // stage the plan through a pinned buffer of the ring
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Stage& sg = ctx->ring[ctx->ring_pos];
-  ctx->ring_pos = (ctx->ring_pos + 1) % kRing;
-  hipError_t e;
-  if (sg.pending) {
-    if ((e = hipEventSynchronize(sg.ev)) != hipSuccess) return device_fail(ctx, "staging event wait", e);
-    sg.pending = false;
-  }
-  if (!sg.ev && (e = hipEventCreateWithFlags(&sg.ev, hipEventDisableTiming)) != hipSuccess)
-    return device_fail(ctx, "hipEventCreate", e);
-  if (sg.cap < plan.blob_bytes) {
-    if (sg.host) hipHostFree(sg.host);
-    sg.host = nullptr;
-    sg.cap = 0;
-    const size_t cap = gkv::align256(plan.blob_bytes * 2);
-    if ((e = hipHostMalloc(&sg.host, cap, hipHostMallocDefault)) != hipSuccess)
-      return device_fail(ctx, "hipHostMalloc(staging)", e);
-    sg.cap = cap;
-  }
-  std::memcpy(sg.host, ctx->blob.data(), plan.blob_bytes);
   const auto t_planned = std::chrono::steady_clock::now();
-  if ((e = hipMemcpyAsync(ctx->ws, sg.host, plan.blob_bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
-    return device_fail(ctx, "work-list copy", e);
-  if ((e = hipEventRecord(sg.ev, st)) != hipSuccess) return device_fail(ctx, "hipEventRecord", e);
-  sg.pending = true;
 
   const Layer& L = ctx->layers[layer];
   uint8_t* ws = static_cast<uint8_t*>(ctx->ws);
-  gkv::StepArgs a{};
   a.batch = batch;
   a.n_q = c.n_q_heads;
   a.n_kv = c.n_kv_heads;
@@ -353,26 +358,27 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   a.v_cold = L.v_cold;
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
   a.cold_indices = cold_indices_d;
-  a.classes = reinterpret_cast<const gkv::PrefixClass*>(ws + plan.off_classes);
-  a.members = reinterpret_cast<const int32_t*>(ws + plan.off_members);
-  a.prefix_items = reinterpret_cast<const gkv::PrefixItem*>(ws + plan.off_prefix);
-  a.n_prefix_items = plan.n_classes > 0 ? plan.n_prefix_items : 0;
-  a.suffix_items = reinterpret_cast<const gkv::SuffixItem*>(ws + plan.off_suffix);
-  a.n_suffix_items = plan.n_suffix_items;
-  a.reqs = reinterpret_cast<const gkv::ReqInfo*>(ws + plan.off_reqs);
-  a.p_o = reinterpret_cast<float*>(ws + off_po);
+  a.p_o = reinterpret_cast<float*>(ws);
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
   a.s_o = reinterpret_cast<float*>(ws + off_so);
   a.s_lse = reinterpret_cast<float*>(ws + off_sl);
-  if ((e = gkv::launch_step(a, c.dtype, backend, st)) != hipSuccess) return device_fail(ctx, "step launch", e);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  hipEvent_t* ev = nullptr;
+  if (ctx->timing_used < ctx->timing_capacity) {
+    ev = &ctx->timing_events[4 * ctx->timing_used];
+    ctx->timing_launched[ctx->timing_used] = (a.prefix_blocks > 0 ? 1 : 0) | 2;
+    ctx->timing_used++;
+  }
+  if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);
 
   ctx->last.backend = backend;
   ctx->last.m_eff = plan.m_eff;
   ctx->last.n_classes = plan.n_classes;
-  ctx->last.n_prefix_blocks = a.n_prefix_items;
-  ctx->last.n_suffix_waves = plan.n_suffix_items;
-  ctx->last.n_suffix_parts = plan.n_chunks;
-  ctx->last.suffix_chunk = plan.suffix_chunk;
+  ctx->last.n_prefix_blocks = plan.prefix_blocks;
+  ctx->last.n_suffix_blocks = plan.suffix_blocks;
+  ctx->last.n_suffix_parts = plan.n_parts;
+  ctx->last.merge_kernel = plan.multi_part;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->have_last = true;

@@ -16,7 +16,10 @@ hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_
                               int32_t cold_cap, hipStream_t stream);
 
 // Prefix kernel of the chosen backend (when there are prefix items), the
-// suffix kernel (when there are suffix items), then the merge.
-hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream);
+// suffix kernel (when there are suffix items), then the merge.  With `ev`
+// non-null, records ev[0] before the first kernel and ev[1], ev[2], ev[3]
+// after the prefix, suffix and merge positions.
+hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
+                       hipEvent_t* ev = nullptr);
 
 }  // namespace gkv

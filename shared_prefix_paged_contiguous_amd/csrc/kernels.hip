@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -60,6 +61,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kLazy = 8.f;   // rescale threshold of the online softmax (log2 units)
 
 // Token of k-slot (lane group g, element e) in a 32-token tile: the tokens
 // whose scores lane group g holds, in the order the S^T accumulators give.
@@ -225,9 +227,14 @@ struct ColState {
     float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
                      fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
     mx = wave_max_groups(mx) * c;
-    const float m_new = fmaxf(m, mx);
-    if (__any(m_new > m)) {   // rescale only when some column's max moved
-      const float alpha = exp2f(m - m_new);
+    // Lazy rescaling: the reference point m only moves when a column's max
+    // exceeds it by more than kLazy (log2 units), so p = 2^(s*c - m) stays
+    // below 2^kLazy and the accumulators are rescaled rarely (the first tile
+    // and genuine jumps), not on every new maximum.  The result is the same:
+    // numerator and denominator share m.
+    if (__any(mx > m + kLazy)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int j = 0; j < TR::EPB; ++j) acc[j] *= alpha;
@@ -236,8 +243,8 @@ struct ColState {
     f32x4 p0, p1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p0[i] = exp2f(__builtin_fmaf(s0[i], c, -m));
-      p1[i] = exp2f(__builtin_fmaf(s1[i], c, -m));
+      p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m));
+      p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m));
     }
     l += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
     TR::pv(acc, vo, p0, p1);
@@ -261,103 +268,318 @@ __device__ __forceinline__ void store_row_slice(float* dst, const float* o, int 
     reinterpret_cast<f32x4*>(dst)[k] = f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
 }
 
+// Joins the partial softmax results of one query head: np parts, part p has
+// base-2 lse lse_of(p) and normalised output row o_of(p) (PER elements per
+// lane at PER*lane).  All loads are issued before any is used.  Writes the
+// joined row through put(acc_scaled) and returns the joined base-2 lse.
+template <int PER, int MB, typename LseF, typename RowF>
+__device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF o_of, float (&acc)[PER]) {
+  auto wave_max = [](float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+  float mx = kNegInf;
+  if (np > MB) {
+    for (int base = 0; base < np; base += 64) mx = fmaxf(mx, base + lane < np ? lse_of(base + lane) : kNegInf);
+    mx = wave_max(mx);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  float wsum = 0.f;
+  for (int base = 0; base < np; base += MB) {
+    const int cnt = min(MB, np - base);
+    const float lp = lane < cnt ? lse_of(base + lane) : kNegInf;
+    float v[MB][PER];
+#pragma unroll
+    for (int k = 0; k < MB; ++k)
+      if (k < cnt) {
+        const float* src = o_of(base + k);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[k][j] = src[j];
+      }
+    if (np <= MB) mx = wave_max(lp);
+    const float wl = lane < cnt && lp != kNegInf ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
+    wsum += wl;
+#pragma unroll
+    for (int k = 0; k < MB; ++k)
+      if (k < cnt) {
+        const float wk = __shfl(wl, k);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += wk * v[k][j];
+      }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] *= inv;
+  return mx + __log2f(wsum);
+}
+
 // ------------------------------------------------------------ suffix kernel
+// One workgroup per (suffix part, KV head); see StepArgs.  Each wave runs
+// the online softmax over its quarter of the part through the slot table,
+// the four results meet in LDS, and the epilogue joins them (and, for a
+// request with a single part, the request's prefix splits) into the output.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void suffix_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void suffix_kernel(StepArgs a) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
-  const int lane = threadIdx.x & 63;
-  const int item_id = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (item_id >= a.n_suffix_items) return;   // no barriers in this kernel
-  const SuffixItem it = a.suffix_items[item_id];
+  constexpr int PER = D / 64;
+  __shared__ int32_t lds_ids[kWaves][kWaveTokens];
+  __shared__ __attribute__((aligned(16))) float lds_o[kWaves][16][D];
+  __shared__ float lds_lse[kWaves][16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int part = blockIdx.x / a.n_kv;
+  const int gk = blockIdx.x - part * a.n_kv;
+  int lo = 0, hi = a.batch - 1;     // rank: last r with part_start[r] <= part
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.part_start[mid] <= part) lo = mid; else hi = mid - 1;
+  }
+  const int b = a.order[lo];
+  const int j = part - a.part_start[lo];
+  const bool single = a.part_start[lo + 1] - a.part_start[lo] == 1;
+  const int tb0 = a.indptr[b], tb1 = a.indptr[b + 1];
+  const int p0 = min(tb1, tb0 + j * kSuffixPart), p1 = min(tb1, p0 + kSuffixPart);
+  const int quarter = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
+  const int w0 = min(p1, p0 + wave * quarter), w1 = min(p1, w0 + quarter);
+  const int len = w1 - w0;
+
   const int n = lane & 15, g = lane >> 4;
-  const bool col_ok = n < a.group;
-  const int h = it.kv_head * a.group + (col_ok ? n : 0);
+  const int G = a.group;
+  const bool col_ok = n < G;
+  const int h = gk * G + (col_ok ? n : 0);
   const float c = a.scale_log2;
 
-  ColState<T, D> st;
-  st.init();
-  if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(it.b) * a.n_q + h) * D, g);
-  else TR::zero_row(st.q);
-
-  const size_t stride = static_cast<size_t>(a.n_kv) * D;
-  const T* kc = static_cast<const T*>(a.k_cold) + it.kv_head * D;
-  const T* vc = static_cast<const T*>(a.v_cold) + it.kv_head * D + TR::EPB * n;
-  const int n_tiles = (it.t1 - it.t0 + kSuffixTile - 1) / kSuffixTile;
-  const int cap1 = a.cold_cap - 1;
-
-  // slot id of token (lane % 32) of tile i (clamped into the tile and the pool)
-  auto load_slot = [&](int i) {
-    const int t = it.t0 + kSuffixTile * i;
-    const int last = min(kSuffixTile, it.t1 - t) - 1;
-    const int s = a.cold_indices[t + min(lane & 31, last)];
-    return min(max(s, 0), cap1);
-  };
-  auto load_kv = [&](int slot, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
-    const int s0 = __shfl(slot, n), s1 = __shfl(slot, 16 + n);
-    TR::load_row(k0, kc + static_cast<size_t>(s0) * stride, g);
-    TR::load_row(k1, kc + static_cast<size_t>(s1) * stride, g);
+  float lse2 = kNegInf;
+  float o[D / 4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int se = __shfl(slot, tau(g, e));
-      v[e] = TR::load_v(vc + static_cast<size_t>(se) * stride);
+  for (int k = 0; k < D / 4; ++k) o[k] = 0.f;
+  if (len > 0) {
+    ColState<T, D> st;
+    st.init();
+    if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
+    else TR::zero_row(st.q);
+
+    const size_t stride = static_cast<size_t>(a.n_kv) * D;
+    const T* kc = static_cast<const T*>(a.k_cold) + gk * D;
+    const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
+    const int n_tiles = (len + kSuffixTile - 1) / kSuffixTile;
+    const int cap1 = a.cold_cap - 1;
+
+    // the quarter's slot ids, clamped into the pool, staged in this wave's
+    // LDS row once: no tile waits on a slot-id load
+    int32_t* ids = lds_ids[wave];
+    for (int k = lane; k < len; k += 64) ids[k] = min(max(a.cold_indices[w0 + k], 0), cap1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    auto load_kv = [&](int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
+      const int base = kSuffixTile * i, last = len - 1;
+      const int s0 = ids[min(base + n, last)], s1 = ids[min(base + 16 + n, last)];
+      TR::load_row(k0, kc + static_cast<size_t>(s0) * stride, g);
+      TR::load_row(k1, kc + static_cast<size_t>(s1) * stride, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int se = ids[min(base + tau(g, e), last)];
+        v[e] = TR::load_v(vc + static_cast<size_t>(se) * stride);
+      }
+    };
+    auto run_tile = [&](const KOp (&k0)[TR::KS], const KOp (&k1)[TR::KS], const VVec (&v)[8], int i) {
+      typename TR::VOp vo;
+      TR::make_vop(vo, v);
+      st.tile(k0, k1, vo, min(kSuffixTile, len - kSuffixTile * i), g, c);
+    };
+
+    // two register sets, alternating: tile i+1 loads while tile i computes
+    KOp ka0[TR::KS], ka1[TR::KS], kb0[TR::KS], kb1[TR::KS];
+    VVec va[8], vb[8];
+    load_kv(0, ka0, ka1, va);
+    for (int i = 0; i < n_tiles; i += 2) {
+      if (i + 1 < n_tiles) load_kv(i + 1, kb0, kb1, vb);
+      run_tile(ka0, ka1, va, i);
+      if (i + 1 >= n_tiles) break;
+      if (i + 2 < n_tiles) load_kv(i + 2, ka0, ka1, va);
+      run_tile(kb0, kb1, vb, i + 1);
     }
-  };
-
-  KOp k0[TR::KS], k1[TR::KS];
-  VVec v[8];
-  load_kv(load_slot(0), k0, k1, v);
-  int slot_next = n_tiles > 1 ? load_slot(1) : 0;
-  for (int i = 0; i < n_tiles; ++i) {
-    KOp nk0[TR::KS], nk1[TR::KS];
-    VVec nv[8];
-    if (i + 1 < n_tiles) load_kv(slot_next, nk0, nk1, nv);
-    if (i + 2 < n_tiles) slot_next = load_slot(i + 2);
-    typename TR::VOp vo;
-    TR::make_vop(vo, v);
-    st.tile(k0, k1, vo, min(kSuffixTile, it.t1 - it.t0 - kSuffixTile * i), g, c);
-    if (i + 1 < n_tiles) {
-#pragma unroll
-      for (int s = 0; s < TR::KS; ++s) { k0[s] = nk0[s]; k1[s] = nk1[s]; }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = nv[e];
-    }
+    lse2 = st.finish(o);
   }
 
-  float o[D / 4];
-  const float lse2 = st.finish(o);
+  // the four quarters meet in LDS
   if (col_ok) {
-    const size_t row = static_cast<size_t>(it.part) * a.n_q + h;
-    store_row_slice(a.s_o + row * D + (D / 4) * g, o, D / 16);
-    if (g == 0) a.s_lse[row] = lse2;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k)
+      *reinterpret_cast<f32x4*>(&lds_o[wave][n][(D / 4) * g + 4 * k]) =
+          f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+    if (g == 0) lds_lse[wave][n] = lse2;
+  }
+  __syncthreads();
+
+  // epilogue: wave w joins columns w, w+4, ...
+  const int cls = a.req_class[b];
+  const int ns = single && cls >= 0 ? a.classes[cls].n_splits : 0;
+  for (int col = wave; col < G; col += kWaves) {
+    const int hc = gk * G + col;
+    const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + hc;
+    float acc[PER];
+    const float l2 = join_parts<PER, 16>(
+        kWaves + ns, lane,
+        [&](int p) { return p < kWaves ? lds_lse[p][col] : a.p_lse[prow0 + static_cast<size_t>(p - kWaves) * a.n_q]; },
+        [&](int p) -> const float* {
+          return p < kWaves ? &lds_o[p][col][PER * lane]
+                            : a.p_o + (prow0 + static_cast<size_t>(p - kWaves) * a.n_q) * D + PER * lane;
+        },
+        acc);
+    if (single) {
+      T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + hc) * D + PER * lane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
+      if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
+    } else {
+      const size_t row = static_cast<size_t>(part) * a.n_q + hc;
+      float* dst = a.s_o + row * D + PER * lane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) dst[k] = acc[k];
+      if (lane == 0) a.s_lse[row] = l2;
+    }
   }
 }
 
 // ------------------------------------------------------------ prefix kernel
+// LDS staging of one 64-token K/V tile.  Threads 0..127 copy K rows as they
+// are; threads 128..255 stage V.  For bf16, a V thread owns lane slot
+// (n, g) of one 32-token half: it loads the 8 token rows tau(g, 0..7) at
+// elements (D/16)*n .., transposes them in registers and writes the D/16
+// A-operand vectors of that lane slot, so the computing waves read their PV
+// operands with one 16-byte LDS read each and no further shuffling.
+template <typename T, int D>
+struct PrefixTileIO {
+  using TR = Traits<T, D>;
+  static constexpr int kKStride = D + 16 / static_cast<int>(sizeof(T));   // padded K row (elements)
+  static constexpr int kChunksPerRow = D * static_cast<int>(sizeof(T)) / 16;
+  static constexpr int kKChunks = kPrefixTile * kChunksPerRow / 128;      // per K thread
+  static constexpr bool kVT = sizeof(T) == 2;                              // V pre-transposed
+  static constexpr int kVBytes = kVT ? 2 * TR::EPB * 64 * 16 : kPrefixTile * kKStride * 4;
+  static constexpr int kKBytes = kPrefixTile * kKStride * static_cast<int>(sizeof(T));
+  static constexpr int kVRegs = kVT ? 8 : kKChunks;   // staged vectors per V thread
+
+  using VStage = typename std::conditional<kVT, typename TR::VVec, u32x4>::type;
+  u32x4 k[kKChunks];
+  VStage v[kVRegs];
+
+  // Thread's first K row and column chunk; its j-th chunk is row
+  // krow + kRowStep * j of the same column (kRowStep = 128 / chunks per row).
+  static constexpr int kRowStep = 128 / kChunksPerRow;
+  static constexpr int kElemsPerChunk = 16 / static_cast<int>(sizeof(T));
+
+  // Global -> registers for the tile starting at token tt.  Rows past t1
+  // (only in the last tile) are clamped to t1 - 1: duplicates, masked later.
+  __device__ void load(const T* kb, const T* vb, int tt, int t1) {
+    const int tid = threadIdx.x;
+    const bool full = tt + kPrefixTile <= t1;
+    if (tid < 128) {
+      const int krow = tid / kChunksPerRow, kcol = tid % kChunksPerRow;
+      if (full) {
+        const T* src = kb + static_cast<size_t>(tt + krow) * D + kcol * kElemsPerChunk;
+#pragma unroll
+        for (int j = 0; j < kKChunks; ++j) k[j] = *reinterpret_cast<const u32x4*>(src + j * kRowStep * D);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kKChunks; ++j)
+          k[j] = *reinterpret_cast<const u32x4*>(
+              kb + static_cast<size_t>(min(tt + krow + j * kRowStep, t1 - 1)) * D + kcol * kElemsPerChunk);
+      }
+    } else if constexpr (kVT) {
+      const int vt = tid - 128, hh = vt >> 6, ls = vt & 63, n = ls & 15, g = ls >> 4;
+      const int r0 = tt + 32 * hh + 4 * g;   // tau(g, e) = 4g + e, or 4g + 12 + e for e >= 4
+      if (full) {
+        const T* src = vb + static_cast<size_t>(r0) * D + TR::EPB * n;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = TR::load_v(src + (e < 4 ? e : 12 + e) * D);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = TR::load_v(vb + static_cast<size_t>(min(r0 + (e < 4 ? e : 12 + e), t1 - 1)) * D + TR::EPB * n);
+      }
+    } else {
+      const int krow = (tid - 128) / kChunksPerRow, kcol = (tid - 128) % kChunksPerRow;
+#pragma unroll
+      for (int j = 0; j < kKChunks; ++j)
+        v[j] = *reinterpret_cast<const u32x4*>(
+            vb + static_cast<size_t>(min(tt + krow + j * kRowStep, t1 - 1)) * D + kcol * kElemsPerChunk);
+    }
+  }
+
+  __device__ void store(T* lk, uint8_t* lv) {
+    const int tid = threadIdx.x;
+    if (tid < 128) {
+      const int krow = tid / kChunksPerRow, kcol = tid % kChunksPerRow;
+#pragma unroll
+      for (int j = 0; j < kKChunks; ++j)
+        *reinterpret_cast<u32x4*>(lk + (krow + j * kRowStep) * kKStride + kcol * kElemsPerChunk) = k[j];
+    } else if constexpr (kVT) {
+      const int vt = tid - 128, hh = vt >> 6, ls = vt & 63;
+      typename TR::VOp vo;
+      TR::make_vop(vo, v);
+#pragma unroll
+      for (int j = 0; j < TR::EPB; ++j)
+        reinterpret_cast<u32x4*>(lv)[(hh * TR::EPB + j) * 64 + ls] = vo.a[j];
+    } else {
+      const int krow = (tid - 128) / kChunksPerRow, kcol = (tid - 128) % kChunksPerRow;
+#pragma unroll
+      for (int j = 0; j < kKChunks; ++j)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(lv) + (krow + j * kRowStep) * kKStride + kcol * 4) = v[j];
+    }
+  }
+
+  // PV operands of half hh for this lane
+  __device__ static void read_vop(typename TR::VOp& vo, const uint8_t* lv, int hh, int lane, int n, int g) {
+    if constexpr (kVT) {
+#pragma unroll
+      for (int j = 0; j < TR::EPB; ++j) vo.a[j] = reinterpret_cast<const u32x4*>(lv)[(hh * TR::EPB + j) * 64 + lane];
+    } else {
+      typename TR::VVec v[8];
+      const float* base = reinterpret_cast<const float*>(lv) + (32 * hh) * kKStride;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = TR::load_v(reinterpret_cast<const T*>(base + tau(g, e) * kKStride + TR::EPB * n));
+      TR::make_vop(vo, v);
+    }
+  }
+};
+
 template <typename T, int D, int RB>
 __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
-  using VVec = typename TR::VVec;
-  constexpr int kStride = D + 16 / static_cast<int>(sizeof(T));   // padded LDS row (elements)
-  constexpr int kChunksPerRow = D * static_cast<int>(sizeof(T)) / 16;
-  constexpr int kChunks = kPrefixTile * kChunksPerRow / kThreads;  // 16-byte chunks per thread
-  constexpr int kElemsPerChunk = 16 / static_cast<int>(sizeof(T));
-  __shared__ __attribute__((aligned(16))) T lds_k[2][kPrefixTile * kStride];
-  __shared__ __attribute__((aligned(16))) T lds_v[2][kPrefixTile * kStride];
+  using IO = PrefixTileIO<T, D>;
+  __shared__ __attribute__((aligned(16))) T lds_k[2][IO::kKBytes / sizeof(T)];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][IO::kVBytes];
 
-  const PrefixItem it = a.prefix_items[blockIdx.x];
-  if (it.cls < 0) return;   // whole workgroup leaves before any barrier
-  const PrefixClass cl = a.classes[it.cls];
-  const int t0 = it.split * cl.chunk;
+  // block -> class, KV head, split, M-tile (see ClassDesc)
+  const int blk = blockIdx.x;
+  int ci = 0;
+  while (ci + 1 < a.n_classes && blk >= a.classes[ci + 1].block_base) ++ci;
+  const ClassDesc& cl = a.classes[ci];
+  const int local = blk - cl.block_base;
+  const int r8 = local / kXcds;
+  const int m_tile = r8 % cl.m_tiles;
+  const int grp = (r8 / cl.m_tiles) * kXcds + local % kXcds;
+  if (grp >= cl.n_groups) return;   // XCD padding: whole workgroup leaves before any barrier
+  const int kv_head = grp / cl.n_splits, split = grp % cl.n_splits;
+  const int t0 = split * cl.chunk;
   const int t1 = min(cl.len, t0 + cl.chunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
   const int rows = cl.n_members * G;
   const float c = a.scale_log2;
-  const int wrow0 = it.row0 + wave * 16 * RB;
+  const int wrow0 = m_tile * 64 * RB + wave * 16 * RB;
   const bool wave_active = wrow0 < rows;
 
   ColState<T, D> st[RB];
@@ -367,67 +589,42 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
     const int r = wrow0 + 16 * rb + n;
     if (r < rows) {
       const int b = a.members[cl.member_off + r / G];
-      const int h = it.kv_head * G + r % G;
+      const int h = kv_head * G + r % G;
       TR::load_row(st[rb].q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
     } else {
       TR::zero_row(st[rb].q);
     }
   }
 
-  const size_t slab = (static_cast<size_t>(it.kv_head) * a.hot_cap + cl.slab_off) * D;
+  const size_t slab = (static_cast<size_t>(kv_head) * a.hot_cap + cl.slab_off) * D;
   const T* kb = static_cast<const T*>(a.k_hot) + slab;
   const T* vb = static_cast<const T*>(a.v_hot) + slab;
   const int n_tiles = (t1 - t0 + kPrefixTile - 1) / kPrefixTile;
 
-  u32x4 stk[kChunks], stv[kChunks];
-  auto stage = [&](int i) {   // global -> registers, rows clamped into [t0, t1)
-    const int tt = t0 + kPrefixTile * i;
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int ch = threadIdx.x + kThreads * j;
-      const int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
-      const size_t off = static_cast<size_t>(min(tt + row, t1 - 1)) * D + col * kElemsPerChunk;
-      stk[j] = *reinterpret_cast<const u32x4*>(kb + off);
-      stv[j] = *reinterpret_cast<const u32x4*>(vb + off);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kChunks; ++j) {
-      const int ch = threadIdx.x + kThreads * j;
-      const int row = ch / kChunksPerRow, col = ch % kChunksPerRow;
-      *reinterpret_cast<u32x4*>(&lds_k[buf][row * kStride + col * kElemsPerChunk]) = stk[j];
-      *reinterpret_cast<u32x4*>(&lds_v[buf][row * kStride + col * kElemsPerChunk]) = stv[j];
-    }
-  };
-
-  stage(0);
-  store(0);
+  IO io;
+  io.load(kb, vb, t0, t1);
+  io.store(lds_k[0], lds_v[0]);
   __syncthreads();
   for (int i = 0; i < n_tiles; ++i) {
     const int buf = i & 1;
-    if (i + 1 < n_tiles) stage(i + 1);
+    if (i + 1 < n_tiles) io.load(kb, vb, t0 + kPrefixTile * (i + 1), t1);
     if (wave_active) {
       const int valid64 = t1 - (t0 + kPrefixTile * i);
 #pragma unroll
       for (int hh = 0; hh < kPrefixTile / 32; ++hh) {
         const int valid = valid64 - 32 * hh;
         if (valid <= 0) break;
-        const T* lk = &lds_k[buf][(32 * hh) * kStride];
-        const T* lv = &lds_v[buf][(32 * hh) * kStride];
+        const T* lk = &lds_k[buf][(32 * hh) * IO::kKStride];
         KOp k0[TR::KS], k1[TR::KS];
-        TR::load_row(k0, lk + n * kStride, g);
-        TR::load_row(k1, lk + (16 + n) * kStride, g);
-        VVec v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = TR::load_v(lv + tau(g, e) * kStride + TR::EPB * n);
+        TR::load_row(k0, lk + n * IO::kKStride, g);
+        TR::load_row(k1, lk + (16 + n) * IO::kKStride, g);
         typename TR::VOp vo;
-        TR::make_vop(vo, v);
+        IO::read_vop(vo, lds_v[buf], hh, lane, n, g);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) st[rb].tile(k0, k1, vo, min(valid, 32), g, c);
       }
     }
-    if (i + 1 < n_tiles) store(buf ^ 1);
+    if (i + 1 < n_tiles) io.store(lds_k[buf ^ 1], lds_v[buf ^ 1]);
     __syncthreads();
   }
 
@@ -439,8 +636,8 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
     const int r = wrow0 + 16 * rb + n;
     if (r < rows) {
       const int b = a.members[cl.member_off + r / G];
-      const int h = it.kv_head * G + r % G;
-      const size_t row = static_cast<size_t>(a.reqs[b].prefix_base) + static_cast<size_t>(it.split) * a.n_q + h;
+      const int h = kv_head * G + r % G;
+      const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + h;
       store_row_slice(a.p_o + row * D + (D / 4) * g, o, D / 16);
       if (g == 0) a.p_lse[row] = lse2;
     }
@@ -448,44 +645,39 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
 }
 
 // ------------------------------------------------------------- merge kernel
+// Requests whose slot table spans several suffix parts: one wave per
+// (request, query head) joins the prefix splits and the part partials.
+// Waves of single-part requests (finished by the suffix kernel) return.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(StepArgs a) {
+  constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
   const int idx = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (idx >= a.batch * a.n_q) return;
   const int b = idx / a.n_q, h = idx % a.n_q;
-  const ReqInfo r = a.reqs[b];
-  const int np = r.n_splits + r.n_chunks;
-  auto lse_of = [&](int p) -> float {
-    return p < r.n_splits ? a.p_lse[r.prefix_base + p * a.n_q + h]
-                          : a.s_lse[(r.chunk_base + p - r.n_splits) * a.n_q + h];
-  };
-  auto o_of = [&](int p) -> const float* {
-    const size_t row = p < r.n_splits ? static_cast<size_t>(r.prefix_base) + static_cast<size_t>(p) * a.n_q + h
-                                      : static_cast<size_t>(r.chunk_base + p - r.n_splits) * a.n_q + h;
-    return (p < r.n_splits ? a.p_o : a.s_o) + row * D;
-  };
-  float mx = kNegInf;
-  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, lse_of(p));
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  constexpr int PER = D / 64;   // output elements per lane
+  const int r = a.rank_of[b];
+  const int c0 = a.part_start[r];
+  const int nparts = a.part_start[r + 1] - c0;
+  if (nparts == 1) return;
+  const int cls = a.req_class[b];
+  const int ns = cls >= 0 ? a.classes[cls].n_splits : 0;
+  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
   float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  float wsum = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float w = exp2f(lse_of(p) - mx);
-    wsum += w;
-    const float* src = o_of(p) + PER * lane;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] += w * src[j];
-  }
-  const float inv = 1.f / wsum;
+  const float l2 = join_parts<PER, 32>(
+      ns + nparts, lane,
+      [&](int p) {
+        return p < ns ? a.p_lse[prow0 + static_cast<size_t>(p) * a.n_q]
+                      : a.s_lse[static_cast<size_t>(c0 + p - ns) * a.n_q + h];
+      },
+      [&](int p) -> const float* {
+        return p < ns ? a.p_o + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
+                      : a.s_o + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane;
+      },
+      acc);
   T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + PER * lane;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) dst[j] = static_cast<T>(acc[j] * inv);
-  if (lane == 0) a.lse[idx] = (mx + __log2f(wsum)) * 0.69314718055994531f;
+  for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
+  if (lane == 0) a.lse[idx] = l2 * 0.69314718055994531f;
 }
 
 // ------------------------------------------------------------ append kernel
@@ -505,22 +697,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, co
 }
 
 template <typename T, int D>
-hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream) {
-  if (a.n_prefix_items > 0) {
+hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
+  if (ev) hipEventRecord(ev[0], stream);
+  if (a.prefix_blocks > 0) {
     if (backend == 2) {
       if constexpr (sizeof(T) == 2) {
-        prefix_kernel<T, D, kDenseRB><<<a.n_prefix_items, kThreads, 0, stream>>>(a);
+        prefix_kernel<T, D, kDenseRB><<<a.prefix_blocks, kThreads, 0, stream>>>(a);
       } else {
         return hipErrorInvalidValue;
       }
     } else {
-      prefix_kernel<T, D, kCascadeRB><<<a.n_prefix_items, kThreads, 0, stream>>>(a);
+      prefix_kernel<T, D, kCascadeRB><<<a.prefix_blocks, kThreads, 0, stream>>>(a);
     }
   }
-  if (a.n_suffix_items > 0)
-    suffix_kernel<T, D><<<(a.n_suffix_items + kWaves - 1) / kWaves, kThreads, 0, stream>>>(a);
-  const int pairs = a.batch * a.n_q;
-  merge_kernel<T, D><<<(pairs + kWaves - 1) / kWaves, kThreads, 0, stream>>>(a);
+  if (ev) hipEventRecord(ev[1], stream);
+  suffix_kernel<T, D><<<a.suffix_blocks, kThreads, 0, stream>>>(a);
+  if (ev) hipEventRecord(ev[2], stream);
+  if (a.multi_part) {
+    const int pairs = a.batch * a.n_q;
+    merge_kernel<T, D><<<(pairs + kWaves - 1) / kWaves, kThreads, 0, stream>>>(a);
+  }
+  if (ev) hipEventRecord(ev[3], stream);
   return hipGetLastError();
 }
 
@@ -540,13 +737,14 @@ hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_
   return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream) {
+hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
+                       hipEvent_t* ev) {
   if (dtype == 1) {
-    return a.head_dim == 128 ? launch_typed<__bf16, 128>(a, backend, stream)
-                             : launch_typed<__bf16, 64>(a, backend, stream);
+    return a.head_dim == 128 ? launch_typed<__bf16, 128>(a, backend, stream, ev)
+                             : launch_typed<__bf16, 64>(a, backend, stream, ev);
   }
-  return a.head_dim == 128 ? launch_typed<float, 128>(a, backend, stream)
-                           : launch_typed<float, 64>(a, backend, stream);
+  return a.head_dim == 128 ? launch_typed<float, 128>(a, backend, stream, ev)
+                           : launch_typed<float, 64>(a, backend, stream, ev);
 }
 
 }  // namespace gkv

@@ -1,6 +1,6 @@
-// Work descriptors of one decode step, shared by the host planner and the
-// device kernels.  Plain structs: the planner writes them into a pinned host
-// buffer, one async copy moves them into the device workspace.
+// Work description of one decode step, shared by the host planner and the
+// device kernels.  The whole description travels in the kernel arguments
+// (about 9 KB), so a step needs no host-to-device copy before its kernels.
 #pragma once
 
 #include <cstdint>
@@ -17,56 +17,51 @@ constexpr int kPrefixTile = 64;
 constexpr int kCascadeRB = 1;     // cascade backend: 64-row tiles, many L splits
 constexpr int kDenseRB = 2;       // dense backend: 128-row tiles (batched GEMM)
 constexpr int kSuffixTile = 32;   // suffix kernel token tile (per wave)
+constexpr int kWaveTokens = 1024; // most slot-table tokens one suffix wave covers (ids staged in LDS)
+constexpr int kSuffixPart = kWaves * kWaveTokens;   // tokens per suffix workgroup
 constexpr int kMaxSplits = 64;    // L splits per prefix class
+constexpr int kXcds = 8;          // MI355X: workgroups go to the 8 XCDs round-robin
+
+// Limits of one step (the description must fit the kernel arguments).
+constexpr int kMaxBatch = 1024;
+constexpr int kMaxClasses = 32;
 
 // One distinct HOT prefix in the step ("class": every request that starts
-// with this slab).
-struct PrefixClass {
+// with this slab).  Its prefix blocks are [block_base, block_base+n_blocks):
+// local block i -> XCD slot x = i % 8, r = i / 8, M-tile r % m_tiles, group
+// (r / m_tiles) * 8 + x, group = kv_head * n_splits + split.  The M-tiles of
+// one group thus share an XCD (and its L2) and are dispatched together.
+struct ClassDesc {
   int64_t slab_off;     // token offset of the slab in the HOT pool
   int32_t len;          // slab length L_c (tokens)
   int32_t n_members;    // requests of the class
-  int32_t member_off;   // first entry in the member list
+  int32_t member_off;   // first entry in members[]
   int32_t n_splits;     // L splits S_c
   int32_t chunk;        // tokens per split (the last split may be shorter)
+  int32_t m_tiles;      // ceil(n_members * G / (64 * RB))
+  int32_t n_groups;     // n_kv * n_splits
+  int32_t block_base;   // first prefix block
+  int32_t n_blocks;     // 8 * ceil(n_groups / 8) * m_tiles
   int32_t pad_;
 };
 
-// One prefix workgroup: rows [row0, row0 + 64*RB) of class `cls` (row r is
-// member r / G, query head kv_head*G + r % G) against tokens
-// [split*chunk, min(len, (split+1)*chunk)) of the slab.  cls < 0: idle
-// (padding of the XCD-aware block order).
-struct PrefixItem {
-  int32_t cls;
-  int32_t kv_head;
-  int32_t row0;
-  int32_t split;
-};
-
-// One suffix wave: request b, KV head kv_head, slot-table positions [t0, t1).
-// Its G query heads write partial rows (part * n_q + h).
-struct SuffixItem {
-  int32_t b;
-  int32_t kv_head;
-  int32_t t0;
-  int32_t t1;
-  int32_t part;
-  int32_t pad_[3];
-};
-
-// Per request: where its partials are, for the merge.
-struct ReqInfo {
-  int32_t cls;          // prefix class, -1 = none
-  int32_t prefix_base;  // prefix partial row of split s, head h: prefix_base + s*n_q + h
-  int32_t n_splits;     // 0 if no prefix
-  int32_t chunk_base;   // first suffix part id
-  int32_t n_chunks;     // suffix parts (0 if the slot table is empty)
-  int32_t pad_[3];
-};
-
-// Everything a step's kernels read, passed by value.
+// Suffix work: one workgroup per (suffix part, KV head).  Requests are
+// ranked longest slot table first; rank r owns parts [part_start[r],
+// part_start[r+1]) (at least one, so every request gets a merge epilogue);
+// part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
+// and the 4 waves take consecutive quarters of it.  Block i -> part
+// i / n_kv, KV head i % n_kv.  A request with one part is finished in the
+// suffix workgroup's epilogue; with several, each part writes a partial and
+// the merge kernel joins them.
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
+  int32_t n_classes;
+  int32_t prefix_blocks;       // sum of class n_blocks
+  int32_t suffix_blocks;       // n_parts * n_kv
+  int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
+  int32_t multi_part;          // some request has more than one suffix part
+  int32_t pad_;
   const void* q;
   void* out;
   float* lse;
@@ -76,18 +71,19 @@ struct StepArgs {
   const void* k_cold;
   const void* v_cold;
   int32_t cold_cap;
-  const int32_t* cold_indices;
-  const PrefixClass* classes;
-  const int32_t* members;
-  const PrefixItem* prefix_items;
-  int32_t n_prefix_items;
-  const SuffixItem* suffix_items;
-  int32_t n_suffix_items;
-  const ReqInfo* reqs;
+  int32_t pad2_;
+  const int32_t* cold_indices; // dev
   float* p_o;                  // prefix partials [rows][head_dim], normalised
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
-  float* s_o;                  // suffix partials
+  float* s_o;                  // multi-part suffix partials, row = part * n_q + h
   float* s_lse;
+  ClassDesc classes[kMaxClasses];
+  int32_t indptr[kMaxBatch + 1];        // slot-table row pointers (host copy of cold_indptr)
+  int32_t part_start[kMaxBatch + 1];    // by rank
+  int16_t order[kMaxBatch];             // request of rank r
+  int16_t rank_of[kMaxBatch];           // rank of request b
+  int16_t members[kMaxBatch];           // requests grouped by class
+  int8_t req_class[kMaxBatch];          // class of request b, -1 = none
 };
 
 }  // namespace gkv

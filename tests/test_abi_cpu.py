@@ -223,9 +223,10 @@ def test_attn_decode_rejects_bad_steps_before_any_device_work():
             c.attn_decode(0, 16, ids, indptr, 16, 16, 16, 16, batch=len(ids), stream=0)
     with pytest.raises(binding.GkvError, match="too small"):
         c2 = _ctx()
+        pid2, _ = c2.hot_pool_alloc(50)          # prefix partials need workspace
         c2.bind_layer(0, 16, 16, 16, 16)
         c2.bind_workspace(256, 256)
-        c2.attn_decode(0, 16, [-1], [0, 3], 16, 16, 16, 16, stream=0)
+        c2.attn_decode(0, 16, [pid2], [0, 3], 16, 16, 16, 16, stream=0)
 
 
 def test_workspace_bound_covers_plans():

@@ -226,3 +226,17 @@ def test_full_size_sampled_requests(name):
     st.run(out2, lse2)
     torch.cuda.synchronize()
     check(out2, lse2, ref_o, ref_l, requests=req)
+
+
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_long_suffixes_span_several_parts(force):
+    """Slot tables longer than one suffix workgroup's share (4096 tokens) are
+    split into parts joined by the merge kernel; mixed with single-part
+    requests and a prefix-only request."""
+    s = spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
+             fixed_suffix=(5000, 10, 0, 9000))
+    w = workloads.make(s)
+    st, out, lse, _ = run(w, force=force)
+    plan = st.ctx.last_plan()
+    assert plan["merge_kernel"] == 1 and plan["n_suffix_parts"] == 2 + 1 + 1 + 3
+    check(out, lse, *oracle_ref(w))
