@@ -74,8 +74,8 @@ typedef struct {
 } gkv_config;
 
 typedef struct {
-  int64_t hot_free_tokens;     /* sum of free HOT extents */
-  int64_t hot_largest_hole;    /* longest free HOT extent */
+  int64_t hot_free_tokens;     /* sum of free HOT extents (whole blocks) */
+  int64_t hot_largest_hole;    /* longest free HOT extent, tokens */
   int32_t hot_live_prefixes;   /* live HOT slabs */
   int32_t hot_free_extents;    /* number of free HOT extents */
   int64_t cold_free_slots;     /* free COLD slots */
@@ -93,13 +93,17 @@ void gkv_destroy(gkv_ctx* ctx);
 /* Last error message of this context ("" if none).  Valid until the next call. */
 const char* gkv_last_error(const gkv_ctx* ctx);
 
-/* Pools of one layer, all dev, contiguous, element type cfg.dtype:
- *   k_hot, v_hot   [n_kv][C_hot][head_dim]   head-major: one (head, prefix)
- *                                            slab is one linear run
+/* Pools of one layer, all dev, element type cfg.dtype, 16-byte aligned:
+ *   k_hot, v_hot   gkv_hot_pool_bytes() bytes each, in the library's blocked
+ *                  layout: per KV head, C_hot / 32 blocks of 32 tokens, each
+ *                  block stored as the register image of the attention
+ *                  kernels' matrix-core operands (V transposed per lane).
+ *                  Head-major, so one (head, prefix) slab is one linear run
+ *                  of whole blocks.  Write rows with gkv_hot_write.
  *   k_cold, v_cold [C_cold][n_kv][head_dim]  token-major: one slot holds one
- *                                            token of every KV head
+ *                  token of every KV head; written with gkv_cold_append.
  * Prefix ids, HOT offsets and COLD slots are shared by all layers.  NULL is
- * allowed for a pool whose capacity is 0. */
+ * allowed for a pool that holds no block / slot. */
 int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot,
                    void* k_cold, void* v_cold);
 
@@ -111,9 +115,21 @@ int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix
  * small host staging ring on first use by a device call. */
 int gkv_bind_workspace(gkv_ctx* ctx, void* dev, size_t bytes);
 
+/* Bytes of one HOT pool buffer (k_hot or v_hot) of one layer. */
+int gkv_hot_pool_bytes(const gkv_ctx* ctx, size_t* bytes);
+
+/* Write rows [token_begin, token_begin + n) of a live slab (the caller's
+ * prefill of a shared prefix).  k_rows, v_rows: dev [n][n_kv][head_dim].
+ * GKV_ERR_NOTFOUND for a dead id, GKV_ERR_INVALID for rows outside the slab.
+ * Asynchronous on `stream`; byte copies into the blocked layout. */
+int gkv_hot_write(gkv_ctx* ctx, int32_t layer, int32_t prefix_id, int32_t token_begin, int32_t n,
+                  const void* k_rows, const void* v_rows, void* stream);
+
 /* HOT pool (paperlayer.ai §3, reading card "Key ideas", Appendix B.8/B.10).
+ * Space is counted in blocks of 32 tokens (the kernels' K/V block): a slab
+ * of n tokens takes ceil(n/32) blocks and starts on a block boundary.
  * First fit over address-ordered free extents; the slab is carved from the
- * start of the lowest-address extent of length >= n_tokens.  Returns the new
+ * start of the lowest-address extent that fits.  Returns the new
  * prefix id (smallest unused non-negative integer) and the slab's token
  * offset.  GKV_ERR_NOSPACE when no single free extent fits - also when the
  * total free space would - with no change to the pool and no demotion of
@@ -195,7 +211,7 @@ typedef struct {
   int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
   int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV heads) */
   int32_t n_suffix_parts;     /* slot-table parts (>= one per request) */
-  int32_t merge_kernel;       /* 1 if a request spanned several parts */
+  int32_t merge_kernel;       /* 1 if the merge kernel ran (a HOT prefix or a multi-part table) */
   int32_t pad_;
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
@@ -203,14 +219,15 @@ typedef struct {
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
 
 /* Per-kernel timing, for measurement.  With capacity > 0, each following
- * gkv_attn_decode records HIP events on its stream before its first kernel
- * and after each of its prefix, suffix and merge kernels, for up to
- * `capacity` calls (then recording stops until read).  capacity 0 disables
- * it and releases the events.  Creating the events is a HIP call. */
+ * gkv_attn_decode records HIP events on its stream before its step kernel
+ * (prefix and suffix work in one launch), after it, and after its merge
+ * kernel, for up to `capacity` calls (then recording stops until read).
+ * capacity 0 disables it and releases the events.  Creating the events is
+ * a HIP call. */
 int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity);
 /* Waits for the recorded calls and writes, per call i, the milliseconds of
- * its prefix, suffix and merge kernels into ms[3i], ms[3i+1], ms[3i+2] (0
- * for a kernel the call did not launch); *n = number of calls written
+ * its step kernel, its merge kernel (0 if not launched) and the whole call
+ * into ms[3i], ms[3i+1], ms[3i+2]; *n = number of calls written
  * (<= max_calls).  Clears the record. */
 int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* n);
 

@@ -16,6 +16,12 @@ the running sum of the lengths, i.e. a plain bump allocator.  A failed
 allocation changes nothing.  Prefix ids are the smallest unused non-negative
 integers.
 
+Granularity (``block``): the pages fix none.  With block = b, space is
+counted in blocks of b tokens: a prefix of n tokens occupies ceil(n / b)
+blocks starting on a block boundary, and a pool of C tokens holds floor(C / b)
+blocks.  block = 1 is the plain reading above; the HIP library allocates in
+blocks of its attention kernels' K/V tile (32 tokens).
+
 COLD pool (paperlayer.ai §3: page size one token; reading card: token-level
 free list).  Reading adopted: a LIFO stack of free slots.  A fresh pool hands
 out 0, 1, 2, ...; ``free(slots)`` pushes the slots in the order given, so the
@@ -35,12 +41,14 @@ class NotFound(Exception):
 
 
 class HotAllocModel:
-    def __init__(self, capacity: int):
-        if capacity < 0:
-            raise ValueError("capacity must be >= 0")
-        self.capacity = int(capacity)
-        self.free_extents = [[0, self.capacity]] if capacity > 0 else []  # [offset, length], address order
-        self.live = {}  # id -> (offset, length)
+    def __init__(self, capacity: int, block: int = 1):
+        if capacity < 0 or block < 1:
+            raise ValueError("capacity must be >= 0 and block >= 1")
+        self.block = int(block)
+        self.capacity = int(capacity) // self.block * self.block
+        # [offset, length] in tokens (multiples of block), address order
+        self.free_extents = [[0, self.capacity]] if self.capacity > 0 else []
+        self.live = {}  # id -> (offset, length in tokens as requested)
 
     def _next_id(self) -> int:
         i = 0
@@ -52,11 +60,12 @@ class HotAllocModel:
         """Return (prefix_id, token_offset) or raise NoSpace (state unchanged)."""
         if n <= 0:
             raise ValueError("n must be >= 1")
+        span = -(-n // self.block) * self.block   # whole blocks
         for ext in self.free_extents:          # lowest address first
-            if ext[1] >= n:
+            if ext[1] >= span:
                 off = ext[0]
-                ext[0] += n
-                ext[1] -= n
+                ext[0] += span
+                ext[1] -= span
                 if ext[1] == 0:
                     self.free_extents.remove(ext)
                 pid = self._next_id()
@@ -68,7 +77,7 @@ class HotAllocModel:
         if pid not in self.live:
             raise NotFound(f"prefix id {pid} is not live")
         off, n = self.live.pop(pid)
-        exts = self.free_extents + [[off, n]]
+        exts = self.free_extents + [[off, -(-n // self.block) * self.block]]
         exts.sort()
         merged = []
         for o, ln in exts:

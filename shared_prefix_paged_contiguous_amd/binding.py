@@ -74,6 +74,8 @@ SIGNATURES = {
     "gkv_bind_layer": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P]),
     "gkv_workspace_size": (ctypes.c_int, [_P, _I32, _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "gkv_bind_workspace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
+    "gkv_hot_pool_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
+    "gkv_hot_write": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "gkv_hot_pool_alloc": (ctypes.c_int, [_P, _I32, _PI32, ctypes.POINTER(_I64)]),
     "gkv_hot_pool_free": (ctypes.c_int, [_P, _I32]),
     "gkv_hot_prefix_info": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I64), _PI32]),
@@ -215,7 +217,19 @@ class Context:
             nbytes = dev.numel() * dev.element_size()
         self._check(self._lib.gkv_bind_workspace(self._h, _ptr(dev), nbytes), "bind_workspace")
 
+    def hot_pool_bytes(self) -> int:
+        b = ctypes.c_size_t()
+        self._check(self._lib.gkv_hot_pool_bytes(self._h, ctypes.byref(b)), "hot_pool_bytes")
+        return b.value
+
     # ------------------------------------------------------------- device ops
+    def hot_write(self, layer: int, prefix_id: int, token_begin: int, k_rows, v_rows,
+                  n: Optional[int] = None, stream=None):
+        if n is None:
+            n = k_rows.shape[0]
+        self._check(self._lib.gkv_hot_write(self._h, layer, prefix_id, token_begin, n, _ptr(k_rows),
+                                            _ptr(v_rows), _stream(stream)), "hot_write")
+
     def cold_append(self, layer: int, k_new, v_new, slots_dev, n: Optional[int] = None, stream=None):
         if n is None:
             n = slots_dev.numel()

@@ -30,6 +30,8 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    # a kernel whose host stub went missing must fail the build, not the load
+    "-Wl,-z,defs",
 ]
 
 

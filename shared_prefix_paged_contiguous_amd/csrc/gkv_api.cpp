@@ -54,7 +54,7 @@ struct gkv_ctx {
 
   explicit gkv_ctx(const gkv_config& c)
       : cfg(c),
-        hot(c.hot_capacity_tokens),
+        hot(c.hot_capacity_tokens, gkv::kHotBlock),
         cold(static_cast<int32_t>(c.cold_capacity_tokens)),
         layers(c.n_layers),
         m_sat(c.m_sat > 0 ? c.m_sat : kDefaultMSat),
@@ -129,7 +129,7 @@ int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot, void* 
   if (!ctx) return GKV_ERR_INVALID;
   if (layer < 0 || layer >= ctx->cfg.n_layers)
     return fail(ctx, GKV_ERR_INVALID, "layer " + std::to_string(layer) + " out of range");
-  if (ctx->cfg.hot_capacity_tokens > 0 && (!k_hot || !v_hot))
+  if (ctx->cfg.hot_capacity_tokens >= gkv::kHotBlock && (!k_hot || !v_hot))
     return fail(ctx, GKV_ERR_INVALID, "HOT pool pointers are NULL");
   if (ctx->cfg.cold_capacity_tokens > 0 && (!k_cold || !v_cold))
     return fail(ctx, GKV_ERR_INVALID, "COLD pool pointers are NULL");
@@ -137,6 +137,36 @@ int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot, void* 
     if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
       return fail(ctx, GKV_ERR_INVALID, "pool pointers must be 16-byte aligned");
   ctx->layers[layer] = Layer{k_hot, v_hot, k_cold, v_cold, true};
+  return GKV_OK;
+}
+
+int gkv_hot_pool_bytes(const gkv_ctx* ctx, size_t* bytes) {
+  if (!ctx || !bytes) return GKV_ERR_INVALID;
+  const gkv_config& c = ctx->cfg;
+  *bytes = static_cast<size_t>(c.n_kv_heads) * static_cast<size_t>(c.hot_capacity_tokens / gkv::kHotBlock) *
+           gkv::kHotBlock * c.head_dim * elem_size(c);
+  return GKV_OK;
+}
+
+int gkv_hot_write(gkv_ctx* ctx, int32_t layer, int32_t prefix_id, int32_t token_begin, int32_t n,
+                  const void* k_rows, const void* v_rows, void* stream) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (int r = check_layer(ctx, layer)) return r;
+  int64_t off;
+  int32_t len;
+  if (!ctx->hot.lookup(prefix_id, &off, &len))
+    return fail(ctx, GKV_ERR_NOTFOUND, "prefix id " + std::to_string(prefix_id) + " is not live");
+  if (n < 0 || token_begin < 0 || static_cast<int64_t>(token_begin) + n > len)
+    return fail(ctx, GKV_ERR_INVALID, "hot_write: rows [" + std::to_string(token_begin) + ", +" +
+                                          std::to_string(n) + ") outside the slab of " + std::to_string(len));
+  if (n == 0) return GKV_OK;
+  if (!k_rows || !v_rows) return fail(ctx, GKV_ERR_INVALID, "hot_write: null rows");
+  const gkv_config& c = ctx->cfg;
+  const Layer& L = ctx->layers[layer];
+  hipError_t e = gkv::launch_hot_write(k_rows, v_rows, n, off + token_begin, c.n_kv_heads, c.head_dim, c.dtype,
+                                       c.hot_capacity_tokens / gkv::kHotBlock, L.k_hot, L.v_hot,
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_fail(ctx, "hot_write launch", e);
   return GKV_OK;
 }
 
@@ -279,18 +309,20 @@ int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* 
   if (!ctx || !n || max_calls < 0 || (max_calls > 0 && !ms)) return GKV_ERR_INVALID;
   const int32_t k = std::min(ctx->timing_used, max_calls);
   for (int32_t i = 0; i < ctx->timing_used; ++i) {
-    hipError_t r = hipEventSynchronize(ctx->timing_events[4 * i + 3]);
+    hipError_t r = hipEventSynchronize(ctx->timing_events[4 * i + 2]);
     if (r != hipSuccess) return device_fail(ctx, "timing event wait", r);
   }
   for (int32_t i = 0; i < k; ++i) {
     hipEvent_t* ev = &ctx->timing_events[4 * i];
-    for (int j = 0; j < 3; ++j) {
-      float t = 0.f;
-      hipError_t r = hipEventElapsedTime(&t, ev[j], ev[j + 1]);
-      if (r != hipSuccess) return device_fail(ctx, "hipEventElapsedTime", r);
-      const bool launched = j == 2 || (ctx->timing_launched[i] >> j & 1);
-      ms[3 * i + j] = launched ? t : 0.f;
-    }
+    float t01 = 0.f, t12 = 0.f, t02 = 0.f;
+    hipError_t r;
+    if ((r = hipEventElapsedTime(&t01, ev[0], ev[1])) != hipSuccess ||
+        (r = hipEventElapsedTime(&t12, ev[1], ev[2])) != hipSuccess ||
+        (r = hipEventElapsedTime(&t02, ev[0], ev[2])) != hipSuccess)
+      return device_fail(ctx, "hipEventElapsedTime", r);
+    ms[3 * i] = t01;
+    ms[3 * i + 1] = (ctx->timing_launched[i] & 2) ? t12 : 0.f;
+    ms[3 * i + 2] = t02;
   }
   *n = k;
   ctx->timing_used = 0;
@@ -353,7 +385,7 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   a.lse = lse;
   a.k_hot = L.k_hot;
   a.v_hot = L.v_hot;
-  a.hot_cap = c.hot_capacity_tokens;
+  a.hot_blocks = c.hot_capacity_tokens / gkv::kHotBlock;
   a.k_cold = L.k_cold;
   a.v_cold = L.v_cold;
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
@@ -367,7 +399,7 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   hipEvent_t* ev = nullptr;
   if (ctx->timing_used < ctx->timing_capacity) {
     ev = &ctx->timing_events[4 * ctx->timing_used];
-    ctx->timing_launched[ctx->timing_used] = (a.prefix_blocks > 0 ? 1 : 0) | 2;
+    ctx->timing_launched[ctx->timing_used] = 1 | (a.need_merge ? 2 : 0);
     ctx->timing_used++;
   }
   if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);

@@ -15,6 +15,12 @@ hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_
                               int32_t n, void* k_cold, void* v_cold, int64_t row_bytes,
                               int32_t cold_cap, hipStream_t stream);
 
+// Scatter n token rows ([n][n_kv][head_dim]) into the blocked HOT layout,
+// starting at pool token tok0 (a slab's offset plus the first row's index).
+hipError_t launch_hot_write(const void* k_rows, const void* v_rows, int32_t n, int64_t tok0, int32_t n_kv,
+                           int32_t head_dim, int32_t dtype, int64_t hot_blocks, void* k_hot, void* v_hot,
+                           hipStream_t stream);
+
 // Prefix kernel of the chosen backend (when there are prefix items), the
 // suffix kernel (when there are suffix items), then the merge.  With `ev`
 // non-null, records ev[0] before the first kernel and ev[1], ev[2], ev[3]

@@ -47,6 +47,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -131,6 +132,24 @@ struct Traits<__bf16, D> {
         o.a[2 * k + 1][j] = __builtin_amdgcn_perm(v[2 * j + 1].w[k], v[2 * j].w[k], 0x07060302u);
       }
   }
+  // Operands from a HOT block image (see the layout note above hot_write_kernel)
+  __device__ static void load_k_img(KOp (&k)[KS], const uint8_t* img, int h, int lane) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k[s] = reinterpret_cast<const u32x4*>(img)[(h * KS + s) * 64 + lane];
+  }
+  __device__ static void load_v_img(VOp& o, const uint8_t* img, int lane) {
+#pragma unroll
+    for (int j = 0; j < EPB; ++j) o.a[j] = reinterpret_cast<const u32x4*>(img)[j * 64 + lane];
+  }
+  // zero the V operand elements of tokens >= valid (element e <-> token tau(g, e))
+  __device__ static void mask_v(VOp& o, int valid, int g) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t m = (tau(g, 2 * w) < valid ? 0x0000ffffu : 0u) | (tau(g, 2 * w + 1) < valid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < EPB; ++j) o.a[j][w] &= m;
+    }
+  }
   __device__ static void pv(f32x4 (&acc)[EPB], const VOp& vo, const f32x4& p0, const f32x4& p1) {
     bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
                  (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
@@ -183,6 +202,25 @@ struct Traits<float, D> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) o.v[e] = v[e];
   }
+  __device__ static void load_k_img(KOp (&k)[KS], const uint8_t* img, int h, int lane) {
+#pragma unroll
+    for (int s4 = 0; s4 < D / 16; ++s4) {
+      const f32x4 x = reinterpret_cast<const f32x4*>(img)[(h * (D / 16) + s4) * 64 + lane];
+      k[4 * s4] = x[0]; k[4 * s4 + 1] = x[1]; k[4 * s4 + 2] = x[2]; k[4 * s4 + 3] = x[3];
+    }
+  }
+  __device__ static void load_v_img(VOp& o, const uint8_t* img, int lane) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      o.v[e] = load_v(reinterpret_cast<const float*>(img) + (e * 64 + lane) * EPB);
+  }
+  __device__ static void mask_v(VOp& o, int valid, int g) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (tau(g, e) >= valid)
+#pragma unroll
+        for (int j = 0; j < EPB; ++j) o.v[e].x[j] = 0.f;
+  }
   // step e contracts the 4 tokens tau(g, e) of the four lane groups
   __device__ static void pv(f32x4 (&acc)[EPB], const VOp& vo, const f32x4& p0, const f32x4& p1) {
 #pragma unroll
@@ -224,16 +262,17 @@ struct ColState {
         if (16 + 4 * g + i >= valid) s1[i] = kNegInf;
       }
     }
-    float mx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                     fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-    mx = wave_max_groups(mx) * c;
-    // Lazy rescaling: the reference point m only moves when a column's max
-    // exceeds it by more than kLazy (log2 units), so p = 2^(s*c - m) stays
-    // below 2^kLazy and the accumulators are rescaled rarely (the first tile
-    // and genuine jumps), not on every new maximum.  The result is the same:
-    // numerator and denominator share m.
-    if (__any(mx > m + kLazy)) {
-      const float m_new = fmaxf(m, mx);
+    // Lazy rescaling: the reference point m of a column only moves when one
+    // of its scores exceeds it by more than kLazy (log2 units), so
+    // p = 2^(s*c - m) < 2^kLazy and the accumulators are rescaled rarely (the
+    // first tile and genuine jumps).  The common path needs no cross-lane
+    // reduction: a wave vote on the lane-local maxima decides; only then is
+    // the column maximum formed (across the four lane groups) and m moved.
+    // Numerator and denominator share m, so the result does not change.
+    const float lmx = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                            fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * c;
+    if (__any(lmx > m + kLazy)) {
+      const float m_new = fmaxf(m, wave_max_groups(lmx));
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
       l *= alpha;
 #pragma unroll
@@ -311,31 +350,46 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  // no tokens in any part (e.g. the suffix quarters of a prefix-only
+  // request): an empty result, o = 0 and lse = -inf, so it weighs nothing
+  if (!(wsum > 0.f)) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    return kNegInf;
+  }
   const float inv = 1.f / wsum;
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] *= inv;
   return mx + __log2f(wsum);
 }
 
-// ------------------------------------------------------------ suffix kernel
+// ------------------------------------------------------------ suffix blocks
 // One workgroup per (suffix part, KV head); see StepArgs.  Each wave runs
-// the online softmax over its quarter of the part through the slot table,
-// the four results meet in LDS, and the epilogue joins them (and, for a
-// request with a single part, the request's prefix splits) into the output.
+// the online softmax over its quarter of the part through the slot table and
+// the four results meet in LDS.  A request without a HOT prefix whose slot
+// table is one part is finished here; otherwise the part's partial is written
+// for the merge kernel.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void suffix_kernel(StepArgs a) {
+struct SuffixSmem {
+  int32_t ids[kWaves][kWaveTokens];
+  float o[kWaves][16][D];
+  float lse[kWaves][16];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
   constexpr int PER = D / 64;
-  __shared__ int32_t lds_ids[kWaves][kWaveTokens];
-  __shared__ __attribute__((aligned(16))) float lds_o[kWaves][16][D];
-  __shared__ float lds_lse[kWaves][16];
+  SuffixSmem<T, D>& sm = *reinterpret_cast<SuffixSmem<T, D>*>(smem_raw);
+  auto& lds_ids = sm.ids;
+  auto& lds_o = sm.o;
+  auto& lds_lse = sm.lse;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int part = blockIdx.x / a.n_kv;
-  const int gk = blockIdx.x - part * a.n_kv;
+  const int part = blk / a.n_kv;
+  const int gk = blk - part * a.n_kv;
   int lo = 0, hi = a.batch - 1;     // rank: last r with part_start[r] <= part
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -421,22 +475,15 @@ void suffix_kernel(StepArgs a) {
   }
   __syncthreads();
 
-  // epilogue: wave w joins columns w, w+4, ...
-  const int cls = a.req_class[b];
-  const int ns = single && cls >= 0 ? a.classes[cls].n_splits : 0;
+  // epilogue: wave w joins columns w, w+4, ... of the four quarters
+  const bool final_here = single && a.req_class[b] < 0;
   for (int col = wave; col < G; col += kWaves) {
     const int hc = gk * G + col;
-    const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + hc;
     float acc[PER];
-    const float l2 = join_parts<PER, 16>(
-        kWaves + ns, lane,
-        [&](int p) { return p < kWaves ? lds_lse[p][col] : a.p_lse[prow0 + static_cast<size_t>(p - kWaves) * a.n_q]; },
-        [&](int p) -> const float* {
-          return p < kWaves ? &lds_o[p][col][PER * lane]
-                            : a.p_o + (prow0 + static_cast<size_t>(p - kWaves) * a.n_q) * D + PER * lane;
-        },
-        acc);
-    if (single) {
+    const float l2 = join_parts<PER, 4>(
+        kWaves, lane, [&](int p) { return lds_lse[p][col]; },
+        [&](int p) -> const float* { return &lds_o[p][col][PER * lane]; }, acc);
+    if (final_here) {
       T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + hc) * D + PER * lane;
 #pragma unroll
       for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
@@ -452,117 +499,90 @@ void suffix_kernel(StepArgs a) {
 }
 
 // ------------------------------------------------------------ prefix kernel
-// LDS staging of one 64-token K/V tile.  Threads 0..127 copy K rows as they
-// are; threads 128..255 stage V.  For bf16, a V thread owns lane slot
-// (n, g) of one 32-token half: it loads the 8 token rows tau(g, 0..7) at
-// elements (D/16)*n .., transposes them in registers and writes the D/16
-// A-operand vectors of that lane slot, so the computing waves read their PV
-// operands with one 16-byte LDS read each and no further shuffling.
+// HOT block images.  A HOT pool stores, per KV head, blocks of kHotBlock = 32
+// tokens; each block is kept as the exact register image of the MFMA
+// operands the attention tile needs, in the order the lanes load them, so a
+// wave fetches every operand with one contiguous 1 KB access:
+//   K image: for half h (tokens 16h..16h+15), k-group s, lane l = n + 16g,
+//            16 bytes = K[16h + n][d of k-group s, lane group g]
+//            (bf16: d = 8g + 32s .. +8; fp32: d = (D/4)g + 4s .. +4);
+//   V image: bf16: for block j < D/16, lane l, the 8 values
+//            V[tau(g, e)][(D/16) n + j], e = 0..7 (V transposed per lane);
+//            fp32: for e < 8, lane l, the D/16 values V[tau(g, e)][(D/16) n ..].
+// gkv_hot_write scatters token rows into this layout.
 template <typename T, int D>
-struct PrefixTileIO {
-  using TR = Traits<T, D>;
-  static constexpr int kKStride = D + 16 / static_cast<int>(sizeof(T));   // padded K row (elements)
-  static constexpr int kChunksPerRow = D * static_cast<int>(sizeof(T)) / 16;
-  static constexpr int kKChunks = kPrefixTile * kChunksPerRow / 128;      // per K thread
-  static constexpr bool kVT = sizeof(T) == 2;                              // V pre-transposed
-  static constexpr int kVBytes = kVT ? 2 * TR::EPB * 64 * 16 : kPrefixTile * kKStride * 4;
-  static constexpr int kKBytes = kPrefixTile * kKStride * static_cast<int>(sizeof(T));
-  static constexpr int kVRegs = kVT ? 8 : kKChunks;   // staged vectors per V thread
-
-  using VStage = typename std::conditional<kVT, typename TR::VVec, u32x4>::type;
-  u32x4 k[kKChunks];
-  VStage v[kVRegs];
-
-  // Thread's first K row and column chunk; its j-th chunk is row
-  // krow + kRowStep * j of the same column (kRowStep = 128 / chunks per row).
-  static constexpr int kRowStep = 128 / kChunksPerRow;
-  static constexpr int kElemsPerChunk = 16 / static_cast<int>(sizeof(T));
-
-  // Global -> registers for the tile starting at token tt.  Rows past t1
-  // (only in the last tile) are clamped to t1 - 1: duplicates, masked later.
-  __device__ void load(const T* kb, const T* vb, int tt, int t1) {
-    const int tid = threadIdx.x;
-    const bool full = tt + kPrefixTile <= t1;
-    if (tid < 128) {
-      const int krow = tid / kChunksPerRow, kcol = tid % kChunksPerRow;
-      if (full) {
-        const T* src = kb + static_cast<size_t>(tt + krow) * D + kcol * kElemsPerChunk;
-#pragma unroll
-        for (int j = 0; j < kKChunks; ++j) k[j] = *reinterpret_cast<const u32x4*>(src + j * kRowStep * D);
-      } else {
-#pragma unroll
-        for (int j = 0; j < kKChunks; ++j)
-          k[j] = *reinterpret_cast<const u32x4*>(
-              kb + static_cast<size_t>(min(tt + krow + j * kRowStep, t1 - 1)) * D + kcol * kElemsPerChunk);
-      }
-    } else if constexpr (kVT) {
-      const int vt = tid - 128, hh = vt >> 6, ls = vt & 63, n = ls & 15, g = ls >> 4;
-      const int r0 = tt + 32 * hh + 4 * g;   // tau(g, e) = 4g + e, or 4g + 12 + e for e >= 4
-      if (full) {
-        const T* src = vb + static_cast<size_t>(r0) * D + TR::EPB * n;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = TR::load_v(src + (e < 4 ? e : 12 + e) * D);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = TR::load_v(vb + static_cast<size_t>(min(r0 + (e < 4 ? e : 12 + e), t1 - 1)) * D + TR::EPB * n);
-      }
-    } else {
-      const int krow = (tid - 128) / kChunksPerRow, kcol = (tid - 128) % kChunksPerRow;
-#pragma unroll
-      for (int j = 0; j < kKChunks; ++j)
-        v[j] = *reinterpret_cast<const u32x4*>(
-            vb + static_cast<size_t>(min(tt + krow + j * kRowStep, t1 - 1)) * D + kcol * kElemsPerChunk);
-    }
+__device__ __forceinline__ void hot_offsets(int tt, int d, int& ko, int& vo) {
+  constexpr int EPB = D / 16;
+  const int h = tt >> 4, nk = tt & 15;
+  const int gl = tt < 16 ? tt >> 2 : (tt - 16) >> 2;     // inverse of tau
+  const int e = tt < 16 ? tt & 3 : 4 + ((tt - 16) & 3);
+  const int nv = d / EPB, j = d % EPB;
+  if constexpr (sizeof(T) == 2) {
+    const int s = d >> 5, dd = d & 31;
+    ko = ((h * (D / 32) + s) * 64 + nk + 16 * (dd >> 3)) * 8 + (dd & 7);
+    vo = (j * 64 + nv + 16 * gl) * 8 + e;
+  } else {
+    const int gk = d / (D / 4), w = d % (D / 4);
+    ko = ((h * (D / 16) + (w >> 2)) * 64 + nk + 16 * gk) * 4 + (w & 3);
+    vo = (e * 64 + nv + 16 * gl) * EPB + j;
   }
+}
 
-  __device__ void store(T* lk, uint8_t* lv) {
-    const int tid = threadIdx.x;
-    if (tid < 128) {
-      const int krow = tid / kChunksPerRow, kcol = tid % kChunksPerRow;
-#pragma unroll
-      for (int j = 0; j < kKChunks; ++j)
-        *reinterpret_cast<u32x4*>(lk + (krow + j * kRowStep) * kKStride + kcol * kElemsPerChunk) = k[j];
-    } else if constexpr (kVT) {
-      const int vt = tid - 128, hh = vt >> 6, ls = vt & 63;
-      typename TR::VOp vo;
-      TR::make_vop(vo, v);
-#pragma unroll
-      for (int j = 0; j < TR::EPB; ++j)
-        reinterpret_cast<u32x4*>(lv)[(hh * TR::EPB + j) * 64 + ls] = vo.a[j];
-    } else {
-      const int krow = (tid - 128) / kChunksPerRow, kcol = (tid - 128) % kChunksPerRow;
-#pragma unroll
-      for (int j = 0; j < kKChunks; ++j)
-        *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(lv) + (krow + j * kRowStep) * kKStride + kcol * 4) = v[j];
-    }
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void hot_write_kernel(const T* k_rows, const T* v_rows, int32_t n,
+                                                             int64_t tok0, int32_t n_kv, int64_t hot_blocks,
+                                                             T* k_hot, T* v_hot) {
+  const int64_t total = static_cast<int64_t>(n) * n_kv * D;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = i / (static_cast<int64_t>(n_kv) * D);
+    const int rem = static_cast<int>(i - t * n_kv * D);
+    const int g = rem / D, d = rem % D;
+    const int64_t tok = tok0 + t;
+    const int64_t img = (static_cast<int64_t>(g) * hot_blocks + tok / kHotBlock) * (kHotBlock * D);
+    int ko, vo;
+    hot_offsets<T, D>(static_cast<int>(tok % kHotBlock), d, ko, vo);
+    k_hot[img + ko] = k_rows[i];
+    v_hot[img + vo] = v_rows[i];
   }
+}
 
-  // PV operands of half hh for this lane
-  __device__ static void read_vop(typename TR::VOp& vo, const uint8_t* lv, int hh, int lane, int n, int g) {
-    if constexpr (kVT) {
-#pragma unroll
-      for (int j = 0; j < TR::EPB; ++j) vo.a[j] = reinterpret_cast<const u32x4*>(lv)[(hh * TR::EPB + j) * 64 + lane];
-    } else {
-      typename TR::VVec v[8];
-      const float* base = reinterpret_cast<const float*>(lv) + (32 * hh) * kKStride;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = TR::load_v(reinterpret_cast<const T*>(base + tau(g, e) * kKStride + TR::EPB * n));
-      TR::make_vop(vo, v);
-    }
-  }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
+// (dst wave-uniform), counted by vmcnt like any vector load.
+__device__ __forceinline__ void load_lds16(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// One prefix workgroup per (class, KV head, M-tile, L split).  The workgroup
+// streams the split's HOT blocks into a ring of kPrefixStages LDS slots with
+// direct global->LDS loads (16 bytes per lane, each block image copied as
+// is), kPrefixStages-1 blocks ahead; every wave reads its MFMA operands from
+// the slot with contiguous 16-byte LDS reads and runs the attention tile for
+// its RB blocks of 16 query rows.  RB = 1 with many L splits is the cascade
+// backend (each slab byte read from HBM once per step; the M-tiles of a
+// split share it through their XCD's L2); RB = 2 is the dense backend
+// (HydraGen-style batched GEMM over M_eff rows with 128-row tiles).
+template <typename T, int D>
+struct PrefixSmem {
+  static constexpr int kImg = kHotBlock * D * static_cast<int>(sizeof(T));   // bytes of one K or V image
+  uint8_t ring[kPrefixStages][2][kImg];
 };
 
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
+__device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
-  using IO = PrefixTileIO<T, D>;
-  __shared__ __attribute__((aligned(16))) T lds_k[2][IO::kKBytes / sizeof(T)];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][IO::kVBytes];
+  constexpr int kImg = PrefixSmem<T, D>::kImg;
+  constexpr int kCopies = kImg / 1024 / kWaves;                        // 1 KB loads per wave per image
+  static_assert(kCopies >= 1, "block image smaller than one load per wave");
+  auto& ring = reinterpret_cast<PrefixSmem<T, D>*>(smem_raw)->ring;
 
   // block -> class, KV head, split, M-tile (see ClassDesc)
-  const int blk = blockIdx.x;
   int ci = 0;
   while (ci + 1 < a.n_classes && blk >= a.classes[ci + 1].block_base) ++ci;
   const ClassDesc& cl = a.classes[ci];
@@ -574,6 +594,7 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
   const int kv_head = grp / cl.n_splits, split = grp % cl.n_splits;
   const int t0 = split * cl.chunk;
   const int t1 = min(cl.len, t0 + cl.chunk);
+  const int nb = (t1 - t0 + kHotBlock - 1) / kHotBlock;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
@@ -596,36 +617,40 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
     }
   }
 
-  const size_t slab = (static_cast<size_t>(kv_head) * a.hot_cap + cl.slab_off) * D;
-  const T* kb = static_cast<const T*>(a.k_hot) + slab;
-  const T* vb = static_cast<const T*>(a.v_hot) + slab;
-  const int n_tiles = (t1 - t0 + kPrefixTile - 1) / kPrefixTile;
-
-  IO io;
-  io.load(kb, vb, t0, t1);
-  io.store(lds_k[0], lds_v[0]);
-  __syncthreads();
-  for (int i = 0; i < n_tiles; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < n_tiles) io.load(kb, vb, t0 + kPrefixTile * (i + 1), t1);
-    if (wave_active) {
-      const int valid64 = t1 - (t0 + kPrefixTile * i);
+  const size_t img0 = (static_cast<size_t>(kv_head) * a.hot_blocks + (cl.slab_off + t0) / kHotBlock) * kImg;
+  const uint8_t* kimg = static_cast<const uint8_t*>(a.k_hot) + img0 + lane * 16;
+  const uint8_t* vimg = static_cast<const uint8_t*>(a.v_hot) + img0 + lane * 16;
+  auto copy = [&](int i) {
+    const int slot = i % kPrefixStages;
 #pragma unroll
-      for (int hh = 0; hh < kPrefixTile / 32; ++hh) {
-        const int valid = valid64 - 32 * hh;
-        if (valid <= 0) break;
-        const T* lk = &lds_k[buf][(32 * hh) * IO::kKStride];
-        KOp k0[TR::KS], k1[TR::KS];
-        TR::load_row(k0, lk + n * IO::kKStride, g);
-        TR::load_row(k1, lk + (16 + n) * IO::kKStride, g);
-        typename TR::VOp vo;
-        IO::read_vop(vo, lds_v[buf], hh, lane, n, g);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) st[rb].tile(k0, k1, vo, min(valid, 32), g, c);
-      }
+    for (int cp = 0; cp < kCopies; ++cp) {
+      const int off = (wave * kCopies + cp) * 1024;
+      load_lds16(kimg + static_cast<size_t>(i) * kImg + off, &ring[slot][0][off]);
+      load_lds16(vimg + static_cast<size_t>(i) * kImg + off, &ring[slot][1][off]);
     }
-    if (i + 1 < n_tiles) io.store(lds_k[buf ^ 1], lds_v[buf ^ 1]);
+  };
+
+  for (int i = 0; i < kPrefixStages - 1 && i < nb; ++i) copy(i);
+  for (int i = 0; i < nb; ++i) {
+    // this wave's copies of block i have landed (later blocks may still fly) ...
+    if (i + kPrefixStages - 2 < nb) wait_vmcnt<(kPrefixStages - 2) * 2 * kCopies>();
+    else wait_vmcnt<0>();
+    // ... and every wave's: block i is in LDS, block i-1's slot is free
     __syncthreads();
+    if (i + kPrefixStages - 1 < nb) copy(i + kPrefixStages - 1);
+    if (wave_active) {
+      const uint8_t* ki = ring[i % kPrefixStages][0];
+      const uint8_t* vi = ring[i % kPrefixStages][1];
+      const int valid = min(kHotBlock, t1 - t0 - kHotBlock * i);
+      KOp k0[TR::KS], k1[TR::KS];
+      TR::load_k_img(k0, ki, 0, lane);
+      TR::load_k_img(k1, ki, 1, lane);
+      typename TR::VOp vo;
+      TR::load_v_img(vo, vi, lane);
+      if (valid < kHotBlock) TR::mask_v(vo, valid, g);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) st[rb].tile(k0, k1, vo, valid, g, c);
+    }
   }
 
   if (!wave_active) return;
@@ -644,10 +669,39 @@ __global__ __launch_bounds__(kThreads) void prefix_kernel(StepArgs a) {
   }
 }
 
+// -------------------------------------------------------------- step kernel
+// Prefix and suffix workgroups of one decode step in one launch.  The grid
+// is a sequence of groups of 8 consecutive blocks (one per XCD); each group
+// is all-prefix or all-suffix, and the two kinds are spread evenly over the
+// sequence, so every CU runs matrix-core-heavy prefix work next to
+// memory-streaming suffix work and neither kind's tail idles the chip.  A
+// prefix block keeps blockIdx % 8 = its index % 8, i.e. its XCD.
+template <typename T, int D>
+constexpr size_t step_smem_bytes() {
+  return sizeof(PrefixSmem<T, D>) > sizeof(SuffixSmem<T, D>) ? sizeof(PrefixSmem<T, D>) : sizeof(SuffixSmem<T, D>);
+}
+
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void step_kernel(StepArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
+  const int groups = (a.prefix_blocks + a.suffix_blocks + kXcds - 1) / kXcds;
+  const int pgroups = a.prefix_blocks / kXcds;       // prefix_blocks is a multiple of 8
+  const int grp = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
+  const int before = static_cast<int>(static_cast<int64_t>(grp) * pgroups / groups);
+  const bool is_prefix = static_cast<int>(static_cast<int64_t>(grp + 1) * pgroups / groups) > before;
+  if (is_prefix) {
+    prefix_block<T, D, RB>(a, before * kXcds + x, smem);
+  } else {
+    const int sb = (grp - before) * kXcds + x;
+    if (sb < a.suffix_blocks) suffix_block<T, D>(a, sb, smem);
+  }
+}
+
 // ------------------------------------------------------------- merge kernel
-// Requests whose slot table spans several suffix parts: one wave per
-// (request, query head) joins the prefix splits and the part partials.
-// Waves of single-part requests (finished by the suffix kernel) return.
+// One wave per (request, query head): joins the request's prefix splits and
+// suffix-part partials.  Requests finished by their suffix block (no HOT
+// prefix, one part) return at once.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(StepArgs a) {
   constexpr int PER = D / 64;
@@ -658,8 +712,8 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(StepArgs a) {
   const int r = a.rank_of[b];
   const int c0 = a.part_start[r];
   const int nparts = a.part_start[r + 1] - c0;
-  if (nparts == 1) return;
   const int cls = a.req_class[b];
+  if (cls < 0 && nparts == 1) return;
   const int ns = cls >= 0 ? a.classes[cls].n_splits : 0;
   const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
   float acc[PER];
@@ -698,26 +752,23 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, co
 
 template <typename T, int D>
 hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
-  if (ev) hipEventRecord(ev[0], stream);
-  if (a.prefix_blocks > 0) {
-    if (backend == 2) {
-      if constexpr (sizeof(T) == 2) {
-        prefix_kernel<T, D, kDenseRB><<<a.prefix_blocks, kThreads, 0, stream>>>(a);
-      } else {
-        return hipErrorInvalidValue;
-      }
+  if (ev) (void)hipEventRecord(ev[0], stream);
+  const int blocks = ((a.prefix_blocks + a.suffix_blocks + kXcds - 1) / kXcds) * kXcds;
+  if (backend == 2) {
+    if constexpr (sizeof(T) == 2) {
+      step_kernel<T, D, kDenseRB><<<blocks, kThreads, 0, stream>>>(a);
     } else {
-      prefix_kernel<T, D, kCascadeRB><<<a.prefix_blocks, kThreads, 0, stream>>>(a);
+      return hipErrorInvalidValue;
     }
+  } else {
+    step_kernel<T, D, kCascadeRB><<<blocks, kThreads, 0, stream>>>(a);
   }
-  if (ev) hipEventRecord(ev[1], stream);
-  suffix_kernel<T, D><<<a.suffix_blocks, kThreads, 0, stream>>>(a);
-  if (ev) hipEventRecord(ev[2], stream);
-  if (a.multi_part) {
+  if (ev) (void)hipEventRecord(ev[1], stream);
+  if (a.need_merge) {
     const int pairs = a.batch * a.n_q;
     merge_kernel<T, D><<<(pairs + kWaves - 1) / kWaves, kThreads, 0, stream>>>(a);
   }
-  if (ev) hipEventRecord(ev[3], stream);
+  if (ev) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();
 }
 
@@ -734,6 +785,25 @@ hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_
   append_kernel<<<grid, kThreads, 0, stream>>>(
       static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new), slots, n,
       static_cast<u32x4*>(k_cold), static_cast<u32x4*>(v_cold), row_chunks, cold_cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_hot_write(const void* k_rows, const void* v_rows, int32_t n, int64_t tok0, int32_t n_kv,
+                           int32_t head_dim, int32_t dtype, int64_t hot_blocks, void* k_hot, void* v_hot,
+                           hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t total = static_cast<int64_t>(n) * n_kv * head_dim;
+  const int grid = static_cast<int>(std::min<int64_t>((total + kThreads - 1) / kThreads, 8192));
+#define GKV_HW(T, D)                                                                                     \
+  hot_write_kernel<T, D><<<grid, kThreads, 0, stream>>>(static_cast<const T*>(k_rows),                  \
+                                                        static_cast<const T*>(v_rows), n, tok0, n_kv,   \
+                                                        hot_blocks, static_cast<T*>(k_hot), static_cast<T*>(v_hot))
+  if (dtype == 1) {
+    if (head_dim == 128) GKV_HW(__bf16, 128); else GKV_HW(__bf16, 64);
+  } else {
+    if (head_dim == 128) GKV_HW(float, 128); else GKV_HW(float, 64);
+  }
+#undef GKV_HW
   return hipGetLastError();
 }
 

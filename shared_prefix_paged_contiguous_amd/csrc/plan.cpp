@@ -177,10 +177,11 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   a.part_start[batch] = static_cast<int32_t>(parts);
   a.suffix_blocks = static_cast<int32_t>(parts * n_kv);
   a.multi_part = multi;
+  a.need_merge = multi || n_classes > 0;
   plan.n_parts = static_cast<int32_t>(parts);
   plan.suffix_blocks = a.suffix_blocks;
-  plan.multi_part = multi;
-  plan.suffix_rows = multi ? parts * n_q : 0;
+  plan.multi_part = a.need_merge;
+  plan.suffix_rows = a.need_merge ? parts * n_q : 0;
   return 0;
 }
 

@@ -20,6 +20,8 @@ constexpr int kSuffixTile = 32;   // suffix kernel token tile (per wave)
 constexpr int kWaveTokens = 1024; // most slot-table tokens one suffix wave covers (ids staged in LDS)
 constexpr int kSuffixPart = kWaves * kWaveTokens;   // tokens per suffix workgroup
 constexpr int kMaxSplits = 64;    // L splits per prefix class
+constexpr int kHotBlock = 32;     // tokens per HOT block; slabs start on block boundaries
+constexpr int kPrefixStages = 4;  // LDS ring depth of the prefix kernel (blocks in flight + 1)
 constexpr int kXcds = 8;          // MI355X: workgroups go to the 8 XCDs round-robin
 
 // Limits of one step (the description must fit the kernel arguments).
@@ -50,9 +52,9 @@ struct ClassDesc {
 // part_start[r+1]) (at least one, so every request gets a merge epilogue);
 // part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
 // and the 4 waves take consecutive quarters of it.  Block i -> part
-// i / n_kv, KV head i % n_kv.  A request with one part is finished in the
-// suffix workgroup's epilogue; with several, each part writes a partial and
-// the merge kernel joins them.
+// i / n_kv, KV head i % n_kv.  A request with no HOT prefix and one part is
+// finished in the suffix workgroup's epilogue; otherwise each part writes a
+// partial and the merge kernel joins them with the request's prefix splits.
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
@@ -61,13 +63,13 @@ struct StepArgs {
   int32_t suffix_blocks;       // n_parts * n_kv
   int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
   int32_t multi_part;          // some request has more than one suffix part
-  int32_t pad_;
+  int32_t need_merge;          // some request has a HOT prefix or several parts
   const void* q;
   void* out;
   float* lse;
-  const void* k_hot;
+  const void* k_hot;           // blocked HOT layout (see gkv_hot_write)
   const void* v_hot;
-  int64_t hot_cap;
+  int64_t hot_blocks;          // HOT blocks per KV head
   const void* k_cold;
   const void* v_cold;
   int32_t cold_cap;
@@ -75,7 +77,7 @@ struct StepArgs {
   const int32_t* cold_indices; // dev
   float* p_o;                  // prefix partials [rows][head_dim], normalised
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
-  float* s_o;                  // multi-part suffix partials, row = part * n_q + h
+  float* s_o;                  // suffix-part partials, row = part * n_q + h
   float* s_lse;
   ClassDesc classes[kMaxClasses];
   int32_t indptr[kMaxBatch + 1];        // slot-table row pointers (host copy of cold_indptr)

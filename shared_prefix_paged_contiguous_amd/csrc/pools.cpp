@@ -4,17 +4,19 @@
 
 namespace gkv {
 
-HotPool::HotPool(int64_t capacity) : capacity_(capacity) {
+HotPool::HotPool(int64_t capacity_tokens, int32_t block)
+    : capacity_(capacity_tokens / block), block_(block) {
   if (capacity_ > 0) free_.emplace(0, capacity_);
 }
 
 int HotPool::alloc(int32_t n, int32_t* id, int64_t* offset) {
+  const int64_t need = (static_cast<int64_t>(n) + block_ - 1) / block_;
   for (auto it = free_.begin(); it != free_.end(); ++it) {   // lowest address first
-    if (it->second < n) continue;
+    if (it->second < need) continue;
     const int64_t off = it->first;
-    const int64_t rest = it->second - n;
+    const int64_t rest = it->second - need;
     free_.erase(it);
-    if (rest > 0) free_.emplace(off + n, rest);
+    if (rest > 0) free_.emplace(off + need, rest);
     int32_t pid;
     if (!released_ids_.empty()) {
       pid = *released_ids_.begin();
@@ -24,7 +26,7 @@ int HotPool::alloc(int32_t n, int32_t* id, int64_t* offset) {
     }
     live_.emplace(pid, Slab{off, n});
     *id = pid;
-    *offset = off;
+    *offset = off * block_;
     return 0;
   }
   return -2;
@@ -34,7 +36,7 @@ int HotPool::release(int32_t id) {
   auto it = live_.find(id);
   if (it == live_.end()) return -3;
   int64_t off = it->second.offset;
-  int64_t len = it->second.len;
+  int64_t len = (static_cast<int64_t>(it->second.len) + block_ - 1) / block_;
   live_.erase(it);
   released_ids_.insert(id);
   // merge with the free extent that ends where this one starts
@@ -60,7 +62,7 @@ int HotPool::release(int32_t id) {
 bool HotPool::lookup(int32_t id, int64_t* offset, int32_t* len) const {
   auto it = live_.find(id);
   if (it == live_.end()) return false;
-  *offset = it->second.offset;
+  *offset = it->second.offset * block_;
   *len = it->second.len;
   return true;
 }
@@ -68,13 +70,13 @@ bool HotPool::lookup(int32_t id, int64_t* offset, int32_t* len) const {
 int64_t HotPool::free_tokens() const {
   int64_t t = 0;
   for (const auto& e : free_) t += e.second;
-  return t;
+  return t * block_;
 }
 
 int64_t HotPool::largest_hole() const {
   int64_t m = 0;
   for (const auto& e : free_) m = std::max(m, e.second);
-  return m;
+  return m * block_;
 }
 
 ColdPool::ColdPool(int32_t capacity)

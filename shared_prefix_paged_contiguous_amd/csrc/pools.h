@@ -8,7 +8,10 @@
 // contiguous extent fits, even if the free total would; live slabs are never
 // demoted).  Free space is a set of address-ordered extents; the last one is
 // the bump region.  Allocation takes the lowest-address extent that fits and
-// carves from its start; freeing merges with free neighbours.
+// carves from its start; freeing merges with free neighbours.  Space is
+// counted in blocks of `block` tokens (the attention kernels' K/V block): a
+// prefix of n tokens takes ceil(n / block) blocks and starts on a block
+// boundary; a pool of C tokens holds floor(C / block) blocks.
 //
 // COLD pool: paperlayer.ai §3 (page size one token); reading card (token-level
 // free list).  A LIFO stack of free slots; a fresh pool hands out 0, 1, 2, ...
@@ -22,7 +25,7 @@
 namespace gkv {
 
 struct HotPool {
-  explicit HotPool(int64_t capacity);
+  HotPool(int64_t capacity_tokens, int32_t block);
 
   // 0 on success; -2 when no extent of n tokens exists (state unchanged).
   int alloc(int32_t n, int32_t* id, int64_t* offset);
@@ -30,9 +33,9 @@ struct HotPool {
   int release(int32_t id);
   bool lookup(int32_t id, int64_t* offset, int32_t* len) const;
 
-  int64_t capacity() const { return capacity_; }
-  int64_t free_tokens() const;
-  int64_t largest_hole() const;
+  int64_t capacity_blocks() const { return capacity_; }
+  int64_t free_tokens() const;      // free blocks x block
+  int64_t largest_hole() const;     // tokens of the longest free extent
   int32_t live_count() const { return static_cast<int32_t>(live_.size()); }
   int32_t extent_count() const { return static_cast<int32_t>(free_.size()); }
 
@@ -41,9 +44,10 @@ struct HotPool {
     int64_t offset;
     int32_t len;
   };
-  int64_t capacity_;
-  std::map<int64_t, int64_t> free_;   // offset -> length, address order
-  std::map<int32_t, Slab> live_;      // id -> slab
+  int64_t capacity_;                  // in blocks
+  int32_t block_;
+  std::map<int64_t, int64_t> free_;   // block offset -> blocks, address order
+  std::map<int32_t, Slab> live_;      // id -> slab (block offset, tokens)
   std::set<int32_t> released_ids_;    // ids below next_id_ that are free again
   int32_t next_id_ = 0;
 };

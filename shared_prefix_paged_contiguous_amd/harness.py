@@ -3,9 +3,10 @@
 Given a ``workloads.Workload`` it creates a library context, replays the
 workload's placement through the context's own allocators (HOT first, COLD
 fallback for prefixes that do not fit, permuted COLD free order for the
-suffix slots), writes the prefix slabs into the HOT pool with torch (the
-caller's prefill, outside the decode path), appends every suffix token into
-the COLD pool with ``cold_append``, and builds the per-request CSR slot table.
+suffix slots), writes the prefix slabs into the HOT pool with ``hot_write``
+(the caller's prefill, outside the decode path), appends every suffix token
+into the COLD pool with ``cold_append``, and builds the per-request CSR slot
+table.
 """
 
 from __future__ import annotations
@@ -45,17 +46,18 @@ class DecodeState:
 
         n_kv, d = s.n_kv, s.head_dim
         dev = torch.device(device)
-        k_hot = torch.zeros((n_kv, max(self.hot_cap, 1), d), dtype=self.dtype, device=dev)
+        hot_elems = max(ctx.hot_pool_bytes() // w.q.element_size(), 16)
+        k_hot = torch.zeros(hot_elems, dtype=self.dtype, device=dev)
         v_hot = torch.zeros_like(k_hot)
         k_cold = torch.zeros((max(self.cold_cap, 1), n_kv, d), dtype=self.dtype, device=dev)
         v_cold = torch.zeros_like(k_cold)
-        for p, ln in enumerate(w.prefix_lens):
-            off = pl["prefix_offset"][p]
-            if off >= 0:
-                k_hot[:, off:off + ln, :] = w.prefix_k[p].to(dev).permute(1, 0, 2)
-                v_hot[:, off:off + ln, :] = w.prefix_v[p].to(dev).permute(1, 0, 2)
         self.pools = [(k_hot, v_hot, k_cold, v_cold)]
         ctx.bind_layer(0, k_hot, v_hot, k_cold, v_cold)
+        # the prefill of each HOT prefix: rows into the slab (blocked layout)
+        for p, ln in enumerate(w.prefix_lens):
+            if pl["prefix_offset"][p] >= 0:
+                ctx.hot_write(0, pl["prefix_id"][p], 0, w.prefix_k[p].to(dev).contiguous(),
+                              w.prefix_v[p].to(dev).contiguous())
 
         # COLD rows: fallen-back prefixes, then every suffix token, via cold_append
         rows_k, rows_v, slots = [], [], []

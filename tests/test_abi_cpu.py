@@ -60,11 +60,16 @@ def test_create_rejects_bad_configs():
             _ctx(**kw)
 
 
+BLOCK = 32   # the library's HOT slab granularity (its kernels' K/V block)
+
+
 def test_hot_pool_matches_hand_trace_and_model():
-    c = _ctx()
-    m = HotAllocModel(100)
-    seq = [("a", 30), ("a", 20), ("a", 40), ("f", 1), ("a", 25), ("a", 15), ("a", 10), ("f", 0),
-           ("f", 2), ("a", 31), ("f", 1), ("f", 1), ("f", 3)]
+    # the model's hand trace scaled to whole blocks: same decisions, offsets x 32
+    c = _ctx(hot_capacity_tokens=100 * BLOCK)
+    m = HotAllocModel(100 * BLOCK, block=BLOCK)
+    seq = [("a", 30 * BLOCK), ("a", 20 * BLOCK), ("a", 40 * BLOCK), ("f", 1), ("a", 25 * BLOCK),
+           ("a", 15 * BLOCK - 7), ("a", 10 * BLOCK), ("f", 0), ("f", 2), ("a", 31 * BLOCK), ("f", 1), ("f", 1),
+           ("f", 3)]
     for op, x in seq:
         if op == "a":
             try:
@@ -91,10 +96,10 @@ def test_hot_pool_matches_hand_trace_and_model():
 
 
 @settings(max_examples=150, deadline=None)
-@given(st.lists(st.tuples(st.sampled_from(["a", "f"]), st.integers(1, 50)), max_size=80))
+@given(st.lists(st.tuples(st.sampled_from(["a", "f"]), st.integers(1, 200)), max_size=80))
 def test_hot_pool_bit_exact_vs_model(seq):
-    c = _ctx(hot_capacity_tokens=160)
-    m = HotAllocModel(160)
+    c = _ctx(hot_capacity_tokens=160 * 4 + 17)
+    m = HotAllocModel(160 * 4 + 17, block=BLOCK)
     for op, x in seq:
         if op == "a":
             try:
@@ -172,7 +177,7 @@ def test_workload_placement_bit_exact_vs_models(name):
         except binding.NoSpace:
             return None
 
-    hm, cm = HotAllocModel(s.hot_capacity), ColdAllocModel(s.cold_capacity)
+    hm, cm = HotAllocModel(s.hot_capacity, block=BLOCK), ColdAllocModel(s.cold_capacity)
 
     def m_hot(n):
         try:
@@ -209,6 +214,7 @@ def test_dispatch_rule_matches_model_and_pages():
 def test_attn_decode_rejects_bad_steps_before_any_device_work():
     c = _ctx()
     pid, _ = c.hot_pool_alloc(10)
+    assert c.hot_pool_bytes() == 2 * (100 // BLOCK) * BLOCK * 64 * 4
     # nothing bound yet
     with pytest.raises(binding.GkvError, match="not bound"):
         c.attn_decode(0, 16, [pid], [0, 0], 0, 0, 16, 16, stream=0)

@@ -65,6 +65,66 @@ def test_cold_append_bit_exact(dtype):
     assert got_v.tobytes() == want_v.tobytes()
 
 
+# --------------------------------------------------------- HOT block layout
+def hot_layout_model(rows_k, rows_v, tok0, n_kv, d, blocks, bf16):
+    """Expected HOT pool contents (element-indexed) after writing token rows
+    [tok0, tok0 + n) of every KV head, from the layout definition: per KV
+    head, blocks of 32 tokens; K image [half h][k-group s][lane n + 16 g][e],
+    V image (bf16) [j][lane][e] with token tau(g, e) = 4g + e (e < 4) or
+    16 + 4g + e - 4, element d = (d/16) n + j; (fp32) [e][lane][j]."""
+    img = 32 * d
+    k = np.zeros(n_kv * blocks * img, dtype=rows_k.dtype)
+    v = np.zeros_like(k)
+    epb = d // 16
+    for t in range(rows_k.shape[0]):
+        tok = tok0 + t
+        blk, tt = divmod(tok, 32)
+        h, nk = divmod(tt, 16)
+        gl, e = (tt // 4, tt % 4) if tt < 16 else ((tt - 16) // 4, 4 + (tt - 16) % 4)
+        for g in range(n_kv):
+            base = (g * blocks + blk) * img
+            for dd in range(d):
+                nv, j = divmod(dd, epb)
+                if bf16:
+                    s, r = divmod(dd, 32)
+                    ko = ((h * (d // 32) + s) * 64 + nk + 16 * (r // 8)) * 8 + r % 8
+                    vo = (j * 64 + nv + 16 * gl) * 8 + e
+                else:
+                    gk, w_ = divmod(dd, d // 4)
+                    ko = ((h * (d // 16) + w_ // 4) * 64 + nk + 16 * gk) * 4 + w_ % 4
+                    vo = (e * 64 + nv + 16 * gl) * epb + j
+                k[base + ko] = rows_k[t, g, dd]
+                v[base + vo] = rows_v[t, g, dd]
+    return k, v
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_hot_write_layout_bit_exact(dtype, d):
+    n_kv, cap = 2, 4 * 32
+    ctx = binding.Context(4, n_kv, d, dtype, cap, 0)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    it = torch.int32 if dtype == "f32" else torch.int16
+    elems = ctx.hot_pool_bytes() // (4 if dtype == "f32" else 2)
+    k_hot = torch.zeros(elems, dtype=td, device="cuda")
+    v_hot = torch.zeros_like(k_hot)
+    ctx.bind_layer(0, k_hot, v_hot, None, None)
+    ctx.hot_pool_alloc(20)                       # block 0
+    pid, off = ctx.hot_pool_alloc(70)            # blocks 1..3
+    assert off == 32
+    g = torch.Generator().manual_seed(3)
+    rk = torch.randn(70, n_kv, d, generator=g).to(td)
+    rv = torch.randn(70, n_kv, d, generator=g).to(td)
+    ctx.hot_write(0, pid, 0, rk[:45].cuda(), rv[:45].cuda())     # two writes, 45 + 25 rows
+    ctx.hot_write(0, pid, 45, rk[45:].cuda(), rv[45:].cuda())
+    torch.cuda.synchronize()
+    want_k, want_v = hot_layout_model(rk.view(it).numpy(), rv.view(it).numpy(), off, n_kv, d, cap // 32,
+                                      dtype == "bf16")
+    assert k_hot.cpu().view(it).numpy().tobytes() == want_k.tobytes()
+    assert v_hot.cpu().view(it).numpy().tobytes() == want_v.tobytes()
+    with pytest.raises(binding.GkvError):
+        ctx.hot_write(0, pid, 60, rk[:11].cuda(), rv[:11].cuda())   # past the slab end
+
+
 # ------------------------------------------------------------- tiny configs
 def test_tiny_fp32_parity():
     w = workloads.make("tiny")
@@ -167,9 +227,9 @@ def test_placement_invariance_is_bitwise():
     w1 = workloads.make(s)
     _, o1, l1, _ = run(w1)
     w2 = dataclasses.replace(w1, cold_perm=np.random.default_rng(5).permutation(s.cold_capacity).astype(np.int32),
-                             hot_churn=[300, 500])   # hole [0,300) too small: slab moves to 800
+                             hot_churn=[300, 500])   # hole [0,320) too small: slab moves to 832
     st2, o2, l2, _ = run(w2)
-    assert st2.placement["prefix_offset"][0] == 800
+    assert st2.placement["prefix_offset"][0] == 832   # 300 and 500 tokens take 10 and 16 blocks of 32
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 

@@ -45,6 +45,23 @@ def test_hot_hand_trace():
     assert h.largest_hole() == 45 and h.free_tokens() == 69
 
 
+def test_hot_block_granularity_hand_trace():
+    # blocks of 32 tokens: a 100-token pool holds 3 blocks (96 tokens)
+    h = HotAllocModel(100, block=32)
+    assert h.free_extents == [[0, 96]]
+    assert h.alloc(33) == (0, 0)          # 2 blocks
+    assert h.alloc(1) == (1, 64)          # 1 block, block-aligned
+    with pytest.raises(NoSpace):
+        h.alloc(1)                        # 96 of 96 tokens taken
+    h.free(0)
+    assert h.free_extents == [[0, 64]]
+    assert h.alloc(64) == (0, 0)          # exactly the freed 2 blocks
+    assert h.live == {0: (0, 64), 1: (64, 1)}
+    h.free(1)
+    h.free(0)
+    assert h.free_extents == [[0, 96]] and h.largest_hole() == 96
+
+
 def test_hot_exact_fit_and_full_pool():
     h = HotAllocModel(10)
     assert h.alloc(10) == (0, 0)
@@ -61,26 +78,28 @@ ops = st.lists(st.tuples(st.sampled_from(["a", "f"]), st.integers(1, 40)), max_s
 
 
 @settings(max_examples=200, deadline=None)
-@given(ops)
-def test_hot_invariants(seq):
+@given(ops, st.sampled_from([1, 4, 32]))
+def test_hot_invariants(seq, block):
     cap = 128
-    h = HotAllocModel(cap)
+    h = HotAllocModel(cap, block=block)
     no_free_yet, running = True, 0
     for kind, n in seq:
         if kind == "a":
             before = ([e[:] for e in h.free_extents], dict(h.live))
-            fits = [e[:] for e in h.free_extents if e[1] >= n]
+            fits = [e[:] for e in h.free_extents]
             try:
                 pid, off = h.alloc(n)
             except NoSpace:
-                assert h.largest_hole() < n                      # NOSPACE iff no hole fits
+                assert h.largest_hole() < -(-n // block) * block  # NOSPACE iff no hole fits
                 assert (h.free_extents, h.live) == before        # and nothing changed
                 continue
-            assert fits and off == fits[0][0]                    # lowest-address fitting hole
+            span = -(-n // block) * block
+            assert off % block == 0
+            assert [e for e in fits if e[1] >= span][0][0] == off    # lowest-address fitting hole
             assert pid == min(set(range(len(h.live) + 1)) - (set(h.live) - {pid}))
             if no_free_yet:
                 assert off == running
-                running += n
+                running += span
         else:
             if not h.live:
                 continue
@@ -88,7 +107,8 @@ def test_hot_invariants(seq):
             h.free(pid)
             no_free_yet = False
         # live slabs and free extents tile [0, cap) exactly, without overlap
-        spans = sorted([list(x) for x in h.live.values()] + [e[:] for e in h.free_extents])
+        spans = sorted([[o, -(-ln // block) * block] for o, ln in h.live.values()] +
+                       [e[:] for e in h.free_extents])
         pos = 0
         for o, ln in spans:
             assert o == pos and ln > 0
