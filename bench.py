@@ -153,6 +153,17 @@ def run_bench(args):
     log(f"[bench] workload={s.name} B={w.batch} replicas={replicas} step_bytes={alg['step_bytes']/1e6:.1f} MB "
         f"setup={time.perf_counter()-t_setup:.1f}s")
 
+    if args.calibrate_copy_mib:
+        # a plain device copy of known size, for scaling HBM byte counters
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: 3 x {args.calibrate_copy_mib} MiB read + written")
+        del src, dst
+
     def step(i):
         layer = i % replicas
         ctx.cold_append(layer, k_new, v_new, slots_new, stream=stream)
@@ -258,7 +269,7 @@ def fit_msat(args):
                 st.ctx.kernel_timing(0)
                 res[label + "_prefix_us"] = round(float(per[:, 2].mean()) * 1e3, 2)   # whole call
                 flops = 4 * bsz * g * w.prefix_lens[0] * w.spec.head_dim * w.spec.n_kv
-                res[label + "_mfma_frac"] = round(flops / (per[:, 0].mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+                res[label + "_mfma_frac"] = round(float(flops / (per[:, 0].mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS), 4)
             rows.append(res)
             print(json.dumps(res), flush=True)
             del st
@@ -283,6 +294,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--fit-msat", action="store_true")
     ap.add_argument("--fit-workloads", default="qwen14b_tp2_lp16k_b128,llama8b_lp16k_b64")
     ap.add_argument("--fit-batches", default="8,16,32,64,128,192,256,384,512")
