@@ -2,8 +2,8 @@
 """Benchmark: one decode step of shared-prefix attention on one MI355X.
 
 A step is the whole hot path for one layer: gkv_cold_append of the batch's
-new tokens into the COLD pool, then gkv_attn_decode (host dispatch, prefix
-kernel of the chosen backend, COLD suffix gather kernel, log-sum-exp merge).
+new tokens into the COLD pool, then gkv_attn_decode (host dispatch, then one step kernel: prefix
+splits of the chosen backend, COLD suffix gather, log-sum-exp join).
 Default workload: Llama-3.1-8B attention shape (32 query / 8 KV heads,
 head_dim 128, bf16), one 16384-token shared prefix in HOT, 64 requests with
 suffixes of 128-1024 tokens scattered token-wise in COLD (seeded N(0,1)
@@ -59,9 +59,9 @@ def algorithmic(w, st):
     q_row = n_q * d * e
     kv_row = n_kv * d * e
     # the step kernel streams every prefix and suffix K/V byte, the slot ids
-    # and q; the merge kernel writes out and lse (partials are overhead)
-    k = {"step": 2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + bsz * q_row,
-         "merge": bsz * q_row + 4 * bsz * n_q}
+    # and q, and writes out and lse (partials are overhead)
+    k = {"step": 2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + bsz * q_row
+         + bsz * q_row + 4 * bsz * n_q}
     append = 2 * 2 * n_suf_req * kv_row + 4 * n_suf_req
     step = (2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + 4 * (bsz + 1)
             + bsz * q_row + bsz * q_row + 4 * bsz * n_q + append)
@@ -201,7 +201,7 @@ def run_bench(args):
         step(i)
     per = ctx.kernel_timing_read(args.steps)
     ctx.kernel_timing(0)
-    kern_ms = {"step": float(per[:, 0].mean()), "merge": float(per[:, 1].mean())}
+    kern_ms = {"step": float(per.mean())}
     log(f"[bench] kernel avg us: " + ", ".join(f"{k}={v*1e3:.1f}" for k, v in kern_ms.items()))
 
     dom = max(kern_ms, key=kern_ms.get)
@@ -230,7 +230,7 @@ def run_bench(args):
         "step_bytes": alg["step_bytes"],
         "warm_ms_per_step": round(ms_warm, 5),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
-        "kernel_note": "step = fused prefix+suffix kernel; merge = LSE merge of splits and parts",
+        "kernel_note": "step = the one kernel of attn_decode: prefix splits, suffix parts and their join",
         "host_plan_us": round(plan["host_plan_us"], 3),
         "roofline": roofline,
     }
@@ -267,9 +267,9 @@ def fit_msat(args):
                     st.run(out, lse, layer=i % 2)
                 per = st.ctx.kernel_timing_read(20)
                 st.ctx.kernel_timing(0)
-                res[label + "_prefix_us"] = round(float(per[:, 2].mean()) * 1e3, 2)   # whole call
+                res[label + "_prefix_us"] = round(float(per.mean()) * 1e3, 2)   # whole call
                 flops = 4 * bsz * g * w.prefix_lens[0] * w.spec.head_dim * w.spec.n_kv
-                res[label + "_mfma_frac"] = round(float(flops / (per[:, 0].mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS), 4)
+                res[label + "_mfma_frac"] = round(float(flops / (per.mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS), 4)
             rows.append(res)
             print(json.dumps(res), flush=True)
             del st

@@ -31,7 +31,8 @@
  *   - Pool bookkeeping calls are host-only and synchronous.  A context is not
  *     thread-safe; callers serialise calls on one context.  Device calls that
  *     share a context's workspace must be issued on one stream (or otherwise
- *     ordered), because each call reuses the workspace.
+ *     ordered): each call reuses the workspace, and the workgroups of one
+ *     call coordinate through counters kept in it.
  *   - Element types: GKV_F32 (float) or GKV_BF16 (bfloat16, round to nearest
  *     even on output).  All arithmetic accumulates in fp32.
  */
@@ -111,8 +112,10 @@ int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot,
  * requests and at most max_suffix_tokens slot-table entries in total. */
 int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix_tokens,
                        size_t* bytes);
-/* Bind caller-owned device workspace (dev, >= 256-byte aligned).  Also pins a
- * small host staging ring on first use by a device call. */
+/* Bind caller-owned device workspace (dev, >= 256-byte aligned).  Host-only:
+ * the first gkv_attn_decode after a bind also enqueues, on its stream, a
+ * small kernel that zeroes the workspace's counter area (partial-join
+ * counters of the step kernel); later calls leave it consistent. */
 int gkv_bind_workspace(gkv_ctx* ctx, void* dev, size_t bytes);
 
 /* Bytes of one HOT pool buffer (k_hot or v_hot) of one layer. */
@@ -211,24 +214,24 @@ typedef struct {
   int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
   int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV heads) */
   int32_t n_suffix_parts;     /* slot-table parts (>= one per request) */
-  int32_t merge_kernel;       /* 1 if the merge kernel ran (a HOT prefix or a multi-part table) */
+  int32_t joins_partials;     /* 1 if some output is joined from several partials (a HOT
+                                 prefix or a multi-part slot table), inside the step kernel */
   int32_t pad_;
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
 } gkv_plan_info;
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
 
-/* Per-kernel timing, for measurement.  With capacity > 0, each following
- * gkv_attn_decode records HIP events on its stream before its step kernel
- * (prefix and suffix work in one launch), after it, and after its merge
- * kernel, for up to `capacity` calls (then recording stops until read).
- * capacity 0 disables it and releases the events.  Creating the events is
- * a HIP call. */
+/* Kernel timing, for measurement.  With capacity > 0, each following
+ * gkv_attn_decode launches its step kernel (prefix splits, suffix parts and
+ * the join of partials, all in one launch) with HIP events that the runtime
+ * stamps with the kernel's own start and end, for up to `capacity` calls
+ * (then recording stops until read).  capacity 0 disables it and releases
+ * the events.  Creating the events is a HIP call. */
 int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity);
-/* Waits for the recorded calls and writes, per call i, the milliseconds of
- * its step kernel, its merge kernel (0 if not launched) and the whole call
- * into ms[3i], ms[3i+1], ms[3i+2]; *n = number of calls written
- * (<= max_calls).  Clears the record. */
+/* Waits for the recorded calls and writes the milliseconds of call i's step
+ * kernel into ms[i]; *n = number of calls written (<= max_calls).  Clears
+ * the record. */
 int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* n);
 
 #ifdef __cplusplus

@@ -56,7 +56,7 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("m_eff", ctypes.c_int32),
                 ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
-                ("merge_kernel", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("joins_partials", ctypes.c_int32), ("pad_", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
 
 
@@ -262,8 +262,8 @@ class Context:
         self._check(self._lib.gkv_kernel_timing(self._h, capacity), "kernel_timing")
 
     def kernel_timing_read(self, max_calls: int) -> np.ndarray:
-        """[calls, 3] milliseconds of the prefix, suffix and merge kernels."""
-        ms = np.zeros((max(max_calls, 1), 3), dtype=np.float32)
+        """[calls] milliseconds of each recorded call's step kernel."""
+        ms = np.zeros(max(max_calls, 1), dtype=np.float32)
         n = ctypes.c_int32()
         self._check(self._lib.gkv_kernel_timing_read(
             self._h, ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), max_calls, ctypes.byref(n)),

@@ -41,14 +41,15 @@ struct gkv_ctx {
   std::vector<Layer> layers;
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  bool ws_clear = false;    // counters of a newly bound workspace still to be zeroed
+  uint32_t done_total[gkv::kMaxClasses] = {};   // completion counter totals per class slot
   int32_t m_sat;
   int32_t force;
   std::string err;
   gkv::StepArgs args;   // kernel-argument block of the current step (~9 KB)
-  std::vector<hipEvent_t> timing_events;   // 4 per recorded call
+  std::vector<hipEvent_t> timing_events;   // 2 per recorded call (kernel start, end)
   int32_t timing_capacity = 0;
   int32_t timing_used = 0;
-  std::vector<int32_t> timing_launched;    // per recorded call: bit 0 prefix, bit 1 suffix
   gkv_plan_info last{};
   bool have_last = false;
 
@@ -70,6 +71,19 @@ int fail(gkv_ctx* ctx, int code, const std::string& msg) {
 
 int device_fail(gkv_ctx* ctx, const char* what, hipError_t e) {
   return fail(ctx, GKV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Counters of the in-kernel join at the start of the workspace: suffix-part
+// arrivals per (request, KV head), which every step leaves at zero, then
+// prefix-split completions per (class slot, KV head), running totals whose
+// per-step targets the host tracks.  Zeroed by the first step on a newly
+// bound workspace.
+size_t part_counter_bytes(const gkv_config& c) {
+  return gkv::align256(static_cast<size_t>(gkv::kMaxBatch) * c.n_kv_heads * sizeof(int32_t));
+}
+size_t counter_bytes(const gkv_config& c) {
+  return part_counter_bytes(c) +
+         gkv::align256(static_cast<size_t>(gkv::kMaxClasses) * c.n_kv_heads * sizeof(int32_t));
 }
 
 size_t elem_size(const gkv_config& c) { return c.dtype == GKV_BF16 ? 2 : 4; }
@@ -176,7 +190,8 @@ int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix
   const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * 4;
   const int64_t pr = gkv::prefix_rows_bound(s, max_batch);
   const int64_t sr = gkv::suffix_rows_bound(s, max_batch, max_suffix_tokens);
-  *bytes = gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) + gkv::align256(sr * 4);
+  *bytes = counter_bytes(ctx->cfg) + gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
+           gkv::align256(sr * 4);
   return GKV_OK;
 }
 
@@ -186,6 +201,7 @@ int gkv_bind_workspace(gkv_ctx* ctx, void* dev, size_t bytes) {
     return fail(ctx, GKV_ERR_INVALID, "workspace must be a non-null 256-byte aligned device pointer");
   ctx->ws = dev;
   ctx->ws_bytes = bytes;
+  ctx->ws_clear = true;   // the first step on it zeroes the counters first
   return GKV_OK;
 }
 
@@ -294,8 +310,7 @@ int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity) {
   ctx->timing_events.clear();
   ctx->timing_capacity = 0;
   ctx->timing_used = 0;
-  ctx->timing_launched.assign(capacity, 0);
-  for (int32_t i = 0; i < 4 * capacity; ++i) {
+  for (int32_t i = 0; i < 2 * capacity; ++i) {
     hipEvent_t e;
     hipError_t r = hipEventCreate(&e);
     if (r != hipSuccess) return device_fail(ctx, "hipEventCreate(timing)", r);
@@ -309,20 +324,15 @@ int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* 
   if (!ctx || !n || max_calls < 0 || (max_calls > 0 && !ms)) return GKV_ERR_INVALID;
   const int32_t k = std::min(ctx->timing_used, max_calls);
   for (int32_t i = 0; i < ctx->timing_used; ++i) {
-    hipError_t r = hipEventSynchronize(ctx->timing_events[4 * i + 2]);
+    hipError_t r = hipEventSynchronize(ctx->timing_events[2 * i + 1]);
     if (r != hipSuccess) return device_fail(ctx, "timing event wait", r);
   }
   for (int32_t i = 0; i < k; ++i) {
-    hipEvent_t* ev = &ctx->timing_events[4 * i];
-    float t01 = 0.f, t12 = 0.f, t02 = 0.f;
-    hipError_t r;
-    if ((r = hipEventElapsedTime(&t01, ev[0], ev[1])) != hipSuccess ||
-        (r = hipEventElapsedTime(&t12, ev[1], ev[2])) != hipSuccess ||
-        (r = hipEventElapsedTime(&t02, ev[0], ev[2])) != hipSuccess)
-      return device_fail(ctx, "hipEventElapsedTime", r);
-    ms[3 * i] = t01;
-    ms[3 * i + 1] = (ctx->timing_launched[i] & 2) ? t12 : 0.f;
-    ms[3 * i + 2] = t02;
+    hipEvent_t* ev = &ctx->timing_events[2 * i];
+    float t01 = 0.f;
+    hipError_t r = hipEventElapsedTime(&t01, ev[0], ev[1]);
+    if (r != hipSuccess) return device_fail(ctx, "hipEventElapsedTime", r);
+    ms[i] = t01;
   }
   *n = k;
   ctx->timing_used = 0;
@@ -361,9 +371,10 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   if (gkv::build_plan(shape_of(c), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
     return fail(ctx, GKV_ERR_INVALID, err);
 
-  // workspace: [prefix o][prefix lse][suffix o][suffix lse]
+  // workspace: [counters][prefix o][prefix lse][suffix o][suffix lse]
   const size_t row = static_cast<size_t>(c.head_dim) * 4;
-  const size_t off_pl = gkv::align256(plan.prefix_rows * row);
+  const size_t off_po = counter_bytes(c);
+  const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
   const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
   const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
   const size_t need = off_sl + gkv::align256(plan.suffix_rows * 4);
@@ -390,7 +401,9 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   a.v_cold = L.v_cold;
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
   a.cold_indices = cold_indices_d;
-  a.p_o = reinterpret_cast<float*>(ws);
+  a.counters = reinterpret_cast<int32_t*>(ws);
+  a.done = reinterpret_cast<uint32_t*>(ws + part_counter_bytes(c));
+  a.p_o = reinterpret_cast<float*>(ws + off_po);
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
   a.s_o = reinterpret_cast<float*>(ws + off_so);
   a.s_lse = reinterpret_cast<float*>(ws + off_sl);
@@ -398,11 +411,22 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   hipError_t e;
   hipEvent_t* ev = nullptr;
   if (ctx->timing_used < ctx->timing_capacity) {
-    ev = &ctx->timing_events[4 * ctx->timing_used];
-    ctx->timing_launched[ctx->timing_used] = 1 | (a.need_merge ? 2 : 0);
+    ev = &ctx->timing_events[2 * ctx->timing_used];
     ctx->timing_used++;
   }
+  if (ctx->ws_clear) {
+    if ((e = gkv::launch_zero_i32(a.counters, counter_bytes(c) / 4, st)) != hipSuccess)
+      return device_fail(ctx, "counter clear launch", e);
+    ctx->ws_clear = false;
+    for (uint32_t& t : ctx->done_total) t = 0;
+  }
+  // every (class slot, KV head) counter gains one count per prefix workgroup
+  // of the class and head: n_splits * m_tiles
+  for (int32_t ci = 0; ci < a.n_classes; ++ci)
+    a.classes[ci].done_target = ctx->done_total[ci] +
+                                static_cast<uint32_t>(a.classes[ci].n_splits) * static_cast<uint32_t>(a.classes[ci].m_tiles);
   if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);
+  for (int32_t ci = 0; ci < a.n_classes; ++ci) ctx->done_total[ci] = a.classes[ci].done_target;
 
   ctx->last.backend = backend;
   ctx->last.m_eff = plan.m_eff;
@@ -410,7 +434,7 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   ctx->last.n_prefix_blocks = plan.prefix_blocks;
   ctx->last.n_suffix_blocks = plan.suffix_blocks;
   ctx->last.n_suffix_parts = plan.n_parts;
-  ctx->last.merge_kernel = plan.multi_part;
+  ctx->last.joins_partials = plan.multi_part;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->have_last = true;

@@ -21,11 +21,13 @@ hipError_t launch_hot_write(const void* k_rows, const void* v_rows, int32_t n, i
                            int32_t head_dim, int32_t dtype, int64_t hot_blocks, void* k_hot, void* v_hot,
                            hipStream_t stream);
 
-// Prefix kernel of the chosen backend (when there are prefix items), the
-// suffix kernel (when there are suffix items), then the merge.  With `ev`
-// non-null, records ev[0] before the first kernel and ev[1], ev[2], ev[3]
-// after the prefix, suffix and merge positions.
+// The step kernel: prefix splits of the chosen backend, suffix parts and the
+// in-kernel join of partials, in one launch.  With `ev` non-null the launch
+// stamps ev[0] / ev[1] with the kernel's start and end.
 hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
                        hipEvent_t* ev = nullptr);
+
+// Zeroes n int32 words at p (a fill kernel, so that it can be captured).
+hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace gkv

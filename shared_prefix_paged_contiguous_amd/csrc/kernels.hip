@@ -27,25 +27,28 @@
 // first product is permuted the same way on both operands.
 //
 // Kernels
-//   suffix_kernel   one wave per (request, KV head, slot-table chunk): gathers
-//                   K/V rows through the slot table (one 16-byte load per
-//                   lane per token row piece, software-pipelined one tile
-//                   ahead), writes a partial per query head.
-//   prefix_kernel   one workgroup per (class, KV head, M-tile, L split):
-//                   streams 64-token K/V tiles of the contiguous slab into
-//                   LDS (double-buffered, 16-byte coalesced loads) and runs
-//                   the MFMA tile for RB 16-row blocks per wave.  RB = 1 with
-//                   many L splits is the cascade backend (each slab byte
-//                   read once per step); RB = 2 with larger M tiles is the
-//                   dense backend (HydraGen-style batched GEMM of M_eff rows).
-//   merge_kernel    one wave per (request, query head): log-sum-exp merge of
-//                   all prefix splits and suffix chunks, writes out and lse.
+//   step_kernel     all attention of one decode step in one launch.  Blocks
+//                   [0, prefix_blocks) are prefix workgroups, one per (class,
+//                   KV head, M-tile, L split): they stream the split's HOT
+//                   blocks into an LDS ring with direct global->LDS loads and
+//                   run the MFMA tile for RB 16-row blocks per wave (RB = 1
+//                   with many L splits: cascade backend, each slab byte read
+//                   once per step; RB = 2: dense backend, HydraGen-style
+//                   batched GEMM of M_eff rows).  The rest are suffix
+//                   workgroups, one per (slot-table part, KV head): they
+//                   gather COLD rows through the slot table (software-
+//                   pipelined one tile ahead) and join their waves' pieces
+//                   in LDS.  Partials are joined by log-sum-exp inside the
+//                   same launch (see StepArgs).
+//   hot_write_kernel  scatter of token rows into the blocked HOT layout.
 //   append_kernel   byte copy of new token rows into COLD slots.
+//   zero_kernel     clears the join counters of a newly bound workspace.
 //
 // Partials keep lse in base 2 of the scaled scores (s * log2(e)/sqrt(d));
-// the merge converts the final lse to natural log.
+// the join converts the final lse to natural log.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cstdint>
@@ -256,10 +259,14 @@ struct ColState {
     f32x4 s0 = TR::qk(k0, q);
     f32x4 s1 = TR::qk(k1, q);
     if (valid < 32) {
+      // partial tile (the last of a range): the compares stay behind the
+      // branch (opaque bound), off the path of full tiles
+      int v = __builtin_amdgcn_readfirstlane(valid);
+      asm volatile("" : "+s"(v));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (4 * g + i >= valid) s0[i] = kNegInf;
-        if (16 + 4 * g + i >= valid) s1[i] = kNegInf;
+        if (4 * g + i >= v) s0[i] = kNegInf;
+        if (16 + 4 * g + i >= v) s1[i] = kNegInf;
       }
     }
     // Lazy rescaling: the reference point m of a column only moves when one
@@ -302,17 +309,48 @@ struct ColState {
   }
 };
 
-__device__ __forceinline__ void store_row_slice(float* dst, const float* o, int n4) {
-  for (int k = 0; k < n4; ++k)
-    reinterpret_cast<f32x4*>(dst)[k] = f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+// Partials cross workgroups (and XCDs, whose L2 caches are not coherent
+// with one another) inside one launch, so they are written and read with
+// agent-scope relaxed atomic accesses: these bypass the non-coherent cache
+// state instead of needing cache-wide write-back / invalidate.  A writer
+// waits for its stores to complete before the arrival that publishes them.
+__device__ __forceinline__ void store_partial(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// n consecutive floats from o to dst (n even, dst 8-byte aligned)
+__device__ __forceinline__ void store_partial_row(float* dst, const float* o, int n) {
+  for (int k = 0; k < n; k += 2) {
+    const uint64_t w = static_cast<uint64_t>(__builtin_bit_cast(uint32_t, o[k])) |
+                       (static_cast<uint64_t>(__builtin_bit_cast(uint32_t, o[k + 1])) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + k), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+__device__ __forceinline__ float load_partial(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int PER>
+__device__ __forceinline__ void load_partial_row(const float* src, float (&v)[PER]) {
+  if constexpr (PER == 2) {
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    v[0] = __builtin_bit_cast(float, static_cast<uint32_t>(w));
+    v[1] = __builtin_bit_cast(float, static_cast<uint32_t>(w >> 32));
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = load_partial(src + j);
+  }
+}
+// all of this wave's partial stores have completed
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 
 // Joins the partial softmax results of one query head: np parts, part p has
-// base-2 lse lse_of(p) and normalised output row o_of(p) (PER elements per
-// lane at PER*lane).  All loads are issued before any is used.  Writes the
-// joined row through put(acc_scaled) and returns the joined base-2 lse.
+// base-2 lse lse_of(p) and normalised output row whose PER elements at
+// PER*lane load_o(p, v) fetches.  All loads of a batch of MB parts are
+// issued before any is used.  Leaves the joined row slice in acc and
+// returns the joined base-2 lse.
 template <int PER, int MB, typename LseF, typename RowF>
-__device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF o_of, float (&acc)[PER]) {
+__device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF load_o, float (&acc)[PER]) {
   auto wave_max = [](float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
@@ -332,11 +370,7 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
     float v[MB][PER];
 #pragma unroll
     for (int k = 0; k < MB; ++k)
-      if (k < cnt) {
-        const float* src = o_of(base + k);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) v[k][j] = src[j];
-      }
+      if (k < cnt) load_o(base + k, v[k]);
     if (np <= MB) mx = wave_max(lp);
     const float wl = lane < cnt && lp != kNegInf ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
     wsum += wl;
@@ -350,7 +384,7 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
-  // no tokens in any part (e.g. the suffix quarters of a prefix-only
+  // no tokens in any part (e.g. the suffix pieces of a prefix-only
   // request): an empty result, o = 0 and lse = -inf, so it weighs nothing
   if (!(wsum > 0.f)) {
 #pragma unroll
@@ -361,6 +395,75 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
 #pragma unroll
   for (int j = 0; j < PER; ++j) acc[j] *= inv;
   return mx + __log2f(wsum);
+}
+
+// ------------------------------------------------------- in-kernel join
+// Partials of request b for query head h: its HOT class's n_splits prefix
+// splits (rows (b * max_splits + s) * n_q + h of p_o / p_lse) and its suffix
+// parts (rows part * n_q + h of s_o / s_lse).  One wave joins them by
+// log-sum-exp and writes out[b][h] (input dtype) and lse[b][h] (natural log).
+template <typename T, int D>
+__device__ __forceinline__ void join_row(const StepArgs& a, int b, int h, int lane) {
+  constexpr int PER = D / 64;
+  const int r = a.rank_of[b];
+  const int c0 = a.part_start[r];
+  const int nparts = a.part_start[r + 1] - c0;
+  const int cls = a.req_class[b];
+  const int ns = cls >= 0 ? a.classes[cls].n_splits : 0;
+  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
+  float acc[PER];
+  const float l2 = join_parts<PER, 32>(
+      ns + nparts, lane,
+      [&](int p) {
+        return load_partial(p < ns ? a.p_lse + prow0 + static_cast<size_t>(p) * a.n_q
+                                   : a.s_lse + static_cast<size_t>(c0 + p - ns) * a.n_q + h);
+      },
+      [&](int p, float (&v)[PER]) {
+        load_partial_row<PER>(p < ns ? a.p_o + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
+                                     : a.s_o + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane,
+                              v);
+      },
+      acc);
+  T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + PER * lane;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
+  if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + h] = l2 * 0.69314718055994531f;
+}
+
+// Counts the arrival of one of request b's suffix parts for KV head g; true
+// for the part that completes the set, which also rewinds the counter to
+// zero for the next call.  Protocol: every wave of the arriving workgroup
+// has stored its partial rows with agent-scope accesses and waited for them
+// to complete, then the workgroup barrier; the arrival is an agent-scope
+// read-modify-write whose result the workgroup waits for, so the workgroup
+// that sees the last count issues its agent-scope partial loads only after
+// every contributor's partials are in place.
+__device__ __forceinline__ bool arrive(const StepArgs& a, int b, int g, int n_parts) {
+  int32_t* cnt = a.counters + static_cast<size_t>(b) * a.n_kv + g;
+  const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool last = old == n_parts - 1;
+  if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Most polls of a completion counter before a wait gives up.  A poll is an
+// agent-scope load plus a short sleep (about a microsecond), so the bound
+// (~0.1 s) is far beyond any step's duration; it only guarantees that the
+// kernel ends even if the counter were never to arrive (the join then reads
+// whatever the partials hold).
+constexpr int kSpinLimit = 1 << 16;
+
+// Waits until every prefix workgroup of class cls and KV head g has
+// published its partials (the class's completion counter reaches its
+// target; the counter is a wrapping running total).  One thread calls it.
+__device__ __forceinline__ void wait_prefix_done(const StepArgs& a, int cls, int g) {
+  const uint32_t* d = a.done + static_cast<size_t>(cls) * a.n_kv + g;
+  const uint32_t target = a.classes[cls].done_target;
+  for (int it = 0; it < kSpinLimit; ++it) {
+    const uint32_t v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<int32_t>(v - target) >= 0) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
 
 // ------------------------------------------------------------ suffix blocks
@@ -377,7 +480,7 @@ struct SuffixSmem {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
+__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw, int32_t& join_flag) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
@@ -400,8 +503,8 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   const bool single = a.part_start[lo + 1] - a.part_start[lo] == 1;
   const int tb0 = a.indptr[b], tb1 = a.indptr[b + 1];
   const int p0 = min(tb1, tb0 + j * kSuffixPart), p1 = min(tb1, p0 + kSuffixPart);
-  const int quarter = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
-  const int w0 = min(p1, p0 + wave * quarter), w1 = min(p1, w0 + quarter);
+  const int piece = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
+  const int w0 = min(p1, p0 + wave * piece), w1 = min(p1, w0 + piece);
   const int len = w1 - w0;
 
   const int n = lane & 15, g = lane >> 4;
@@ -426,7 +529,7 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     const int n_tiles = (len + kSuffixTile - 1) / kSuffixTile;
     const int cap1 = a.cold_cap - 1;
 
-    // the quarter's slot ids, clamped into the pool, staged in this wave's
+    // the piece's slot ids, clamped into the pool, staged in this wave's
     // LDS row once: no tile waits on a slot-id load
     int32_t* ids = lds_ids[wave];
     for (int k = lane; k < len; k += 64) ids[k] = min(max(a.cold_indices[w0 + k], 0), cap1);
@@ -451,21 +554,31 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       st.tile(k0, k1, vo, min(kSuffixTile, len - kSuffixTile * i), g, c);
     };
 
-    // two register sets, alternating: tile i+1 loads while tile i computes
-    KOp ka0[TR::KS], ka1[TR::KS], kb0[TR::KS], kb1[TR::KS];
-    VVec va[8], vb[8];
-    load_kv(0, ka0, ka1, va);
-    for (int i = 0; i < n_tiles; i += 2) {
-      if (i + 1 < n_tiles) load_kv(i + 1, kb0, kb1, vb);
-      run_tile(ka0, ka1, va, i);
-      if (i + 1 >= n_tiles) break;
-      if (i + 2 < n_tiles) load_kv(i + 2, ka0, ka1, va);
-      run_tile(kb0, kb1, vb, i + 1);
+    if constexpr (sizeof(T) * D <= 256) {
+      // two register sets, alternating: tile i+1 loads while tile i computes
+      KOp ka0[TR::KS], ka1[TR::KS], kb0[TR::KS], kb1[TR::KS];
+      VVec va[8], vb[8];
+      load_kv(0, ka0, ka1, va);
+      for (int i = 0; i < n_tiles; i += 2) {
+        if (i + 1 < n_tiles) load_kv(i + 1, kb0, kb1, vb);
+        run_tile(ka0, ka1, va, i);
+        if (i + 1 >= n_tiles) break;
+        if (i + 2 < n_tiles) load_kv(i + 2, ka0, ka1, va);
+        run_tile(kb0, kb1, vb, i + 1);
+      }
+    } else {
+      // fp32 rows of 128: two sets would not fit the register file
+      KOp k0[TR::KS], k1[TR::KS];
+      VVec v[8];
+      for (int i = 0; i < n_tiles; ++i) {
+        load_kv(i, k0, k1, v);
+        run_tile(k0, k1, v, i);
+      }
     }
     lse2 = st.finish(o);
   }
 
-  // the four quarters meet in LDS
+  // the wave pieces meet in LDS
   if (col_ok) {
 #pragma unroll
     for (int k = 0; k < D / 16; ++k)
@@ -475,14 +588,18 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   }
   __syncthreads();
 
-  // epilogue: wave w joins columns w, w+4, ... of the four quarters
+  // epilogue: wave w joins columns w, w+4, ... over the four pieces
   const bool final_here = single && a.req_class[b] < 0;
   for (int col = wave; col < G; col += kWaves) {
     const int hc = gk * G + col;
     float acc[PER];
     const float l2 = join_parts<PER, 4>(
         kWaves, lane, [&](int p) { return lds_lse[p][col]; },
-        [&](int p) -> const float* { return &lds_o[p][col][PER * lane]; }, acc);
+        [&](int p, float (&v)[PER]) {
+#pragma unroll
+          for (int j = 0; j < PER; ++j) v[j] = lds_o[p][col][PER * lane + j];
+        },
+        acc);
     if (final_here) {
       T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + hc) * D + PER * lane;
 #pragma unroll
@@ -490,12 +607,32 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
     } else {
       const size_t row = static_cast<size_t>(part) * a.n_q + hc;
-      float* dst = a.s_o + row * D + PER * lane;
+      if constexpr (PER % 2 == 0) {
+        store_partial_row(a.s_o + row * D + PER * lane, acc, PER);
+      } else {
 #pragma unroll
-      for (int k = 0; k < PER; ++k) dst[k] = acc[k];
-      if (lane == 0) a.s_lse[row] = l2;
+        for (int k = 0; k < PER; ++k) store_partial(a.s_o + row * D + PER * lane + k, acc[k]);
+      }
+      if (lane == 0) store_partial(a.s_lse + row, l2);
     }
   }
+  if (final_here) return;
+
+  // This part's partial is written.  The last of the request's parts to
+  // arrive (for this KV head) waits for the request's prefix splits, if
+  // any, and joins all partials.
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int n_parts = a.part_start[lo + 1] - a.part_start[lo];
+    const bool go = n_parts == 1 || arrive(a, b, gk, n_parts);
+    const int cls = a.req_class[b];
+    if (go && cls >= 0) wait_prefix_done(a, cls, gk);
+    join_flag = go ? 1 : 0;
+  }
+  __syncthreads();
+  if (join_flag == 0) return;
+  for (int col = wave; col < G; col += kWaves) join_row<T, D>(a, b, gk * G + col, lane);
 }
 
 // ------------------------------------------------------------ prefix kernel
@@ -552,35 +689,78 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
-// (dst wave-uniform), counted by vmcnt like any vector load.
-__device__ __forceinline__ void load_lds16(const uint8_t* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// Waits until at most n blocks of C direct-to-LDS loads each (issued after
+// the block waited for) are still in flight, 0 <= n <= NMAX; loads retire in
+// issue order, so older blocks have then landed.
+template <int C, int NMAX>
+__device__ __forceinline__ void wait_blocks_after(int n) {
+  if constexpr (NMAX > 0) {
+    if (n >= NMAX) {
+      wait_vmcnt<NMAX * C>();
+      return;
+    }
+    wait_blocks_after<C, NMAX - 1>(n);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Direct global->LDS copy of 1 KB per wave: lane l moves the 16 bytes at
+// base + voff (voff = 16 l + a per-wave constant) to LDS address lds + 16 l
+// (base and lds wave-uniform).  Counted by vmcnt like any vector load.
+// Issued as inline assembly so that the compiler's own wait-count
+// bookkeeping does not see these transfers: the kernel orders them with
+// explicit vmcnt waits, and the compiler's conservative view of them would
+// otherwise drain the whole ring at some loop barriers.  The compiler's
+// waits for other loads stay correct, only more conservative: vector loads
+// retire in issue order.
+__device__ __forceinline__ void load_lds_1k(uint32_t voff, const uint8_t* base, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const uint8_t*)(p)));
 }
 
 // One prefix workgroup per (class, KV head, M-tile, L split).  The workgroup
-// streams the split's HOT blocks into a ring of kPrefixStages LDS slots with
-// direct global->LDS loads (16 bytes per lane, each block image copied as
-// is), kPrefixStages-1 blocks ahead; every wave reads its MFMA operands from
-// the slot with contiguous 16-byte LDS reads and runs the attention tile for
-// its RB blocks of 16 query rows.  RB = 1 with many L splits is the cascade
-// backend (each slab byte read from HBM once per step; the M-tiles of a
-// split share it through their XCD's L2); RB = 2 is the dense backend
-// (HydraGen-style batched GEMM over M_eff rows with 128-row tiles).
+// streams the split's HOT blocks into an LDS ring with direct global->LDS
+// loads (16 bytes per lane, each block image copied as is), several blocks
+// ahead; every wave reads its MFMA operands from the ring with contiguous
+// 16-byte LDS reads and runs the attention tile for its RB blocks of 16 query
+// rows.  One tile spans 64*RB rows, so a class of up to that many rows per
+// KV head reads each slab byte from HBM exactly once per step.  RB = 1 with
+// many L splits is the cascade backend; RB = 2 is the dense backend
+// (HydraGen-style batched GEMM over M_eff rows with 128-row tiles, tiles of
+// one split sharing it through their XCD's L2).
 template <typename T, int D>
 struct PrefixSmem {
   static constexpr int kImg = kHotBlock * D * static_cast<int>(sizeof(T));   // bytes of one K or V image
-  uint8_t ring[kPrefixStages][2][kImg];
+  // ring depth: what kRingBytes holds, at least 3 (fp32 rows of 128 take
+  // more LDS) and at most 8
+  static constexpr int kFit = kRingBytes / (2 * kImg);
+  static constexpr int kStages = kFit > 8 ? 8 : (kFit < 3 ? 3 : kFit);
+  // a block's K and V images are 2*kImg bytes, copied in 1 KB pieces spread
+  // evenly over the waves
+  static constexpr int kCopies = 2 * kImg / 1024 / kWaves;
+  static_assert(kStages >= 3, "LDS ring too shallow");
+  static_assert(kCopies >= 1 && kCopies * kWaves * 1024 == 2 * kImg, "block images must split evenly over waves");
+  uint8_t ring[kStages][2 * kImg];
 };
 
 template <typename T, int D, int RB>
 __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
-  constexpr int kImg = PrefixSmem<T, D>::kImg;
-  constexpr int kCopies = kImg / 1024 / kWaves;                        // 1 KB loads per wave per image
-  static_assert(kCopies >= 1, "block image smaller than one load per wave");
-  auto& ring = reinterpret_cast<PrefixSmem<T, D>*>(smem_raw)->ring;
+  using SM = PrefixSmem<T, D>;
+  constexpr int kImg = SM::kImg, kStages = SM::kStages, kCopies = SM::kCopies;
+  auto& ring = reinterpret_cast<SM*>(smem_raw)->ring;
 
   // block -> class, KV head, split, M-tile (see ClassDesc)
   int ci = 0;
@@ -595,87 +775,217 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   const int t0 = split * cl.chunk;
   const int t1 = min(cl.len, t0 + cl.chunk);
   const int nb = (t1 - t0 + kHotBlock - 1) / kHotBlock;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
-  const int rows = cl.n_members * G;
+  // the tile's requests: members [mem0, mem0 + n_mem) of the class, rows
+  // r = i * G + j (member mem0 + i, query head kv_head * G + j)
+  const int tm = tile_members(G, RB);
+  const int mem0 = m_tile * tm;
+  const int n_mem = min(tm, cl.n_members - mem0);
+  const int rows = n_mem * G;
   const float c = a.scale_log2;
-  const int wrow0 = m_tile * 64 * RB + wave * 16 * RB;
+  const int wrow0 = wave * 16 * RB;
   const bool wave_active = wrow0 < rows;
 
+  // K image at ring[slot][0, kImg), V image at ring[slot][kImg, 2 kImg).  A
+  // block's images are kImg bytes each in the separate K and V pools; copy
+  // cp of a wave moves the 1 KB piece at offset (cp * kWaves + wave) KB of
+  // the pair.  Sources and LDS targets are wave-uniform (scalar) addresses;
+  // the per-lane 16-byte offset is the same for every copy.
+  const size_t img0 = (static_cast<size_t>(kv_head) * a.hot_blocks + (cl.slab_off + t0) / kHotBlock) * kImg;
+  const uint8_t* src0[kCopies];
+  uint32_t dst0[kCopies];
+  const uint32_t ring_lds = lds_addr(&ring[0][0]);
+#pragma unroll
+  for (int cp = 0; cp < kCopies; ++cp) {
+    const int off = (cp * kWaves + wave) * 1024;
+    src0[cp] = off < kImg ? static_cast<const uint8_t*>(a.k_hot) + img0 + off
+                          : static_cast<const uint8_t*>(a.v_hot) + img0 + (off - kImg);
+    dst0[cp] = ring_lds + off;
+  }
+  const uint32_t voff = static_cast<uint32_t>(lane) * 16;
+  // copies block i into ring slot `slot`
+  auto copy = [&](int i, int slot) {
+#pragma unroll
+    for (int cp = 0; cp < kCopies; ++cp)
+      load_lds_1k(voff, src0[cp] + static_cast<size_t>(i) * kImg, dst0[cp] + slot * (2 * kImg));
+  };
   ColState<T, D> st[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     st[rb].init();
     const int r = wrow0 + 16 * rb + n;
     if (r < rows) {
-      const int b = a.members[cl.member_off + r / G];
+      const int b = a.members[cl.member_off + mem0 + r / G];
       const int h = kv_head * G + r % G;
       TR::load_row(st[rb].q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
     } else {
       TR::zero_row(st[rb].q);
     }
   }
-
-  const size_t img0 = (static_cast<size_t>(kv_head) * a.hot_blocks + (cl.slab_off + t0) / kHotBlock) * kImg;
-  const uint8_t* kimg = static_cast<const uint8_t*>(a.k_hot) + img0 + lane * 16;
-  const uint8_t* vimg = static_cast<const uint8_t*>(a.v_hot) + img0 + lane * 16;
-  auto copy = [&](int i) {
-    const int slot = i % kPrefixStages;
+  // The first kStages - 1 copies fly while the query rows land.  Their
+  // number is fixed (slots past the last block get a spare copy of it, never
+  // read), and the query registers are claimed right after them: the
+  // compiler's wait for the query loads is then placed here with an exact
+  // count and none remains inside the loop, where it would drain the ring.
 #pragma unroll
-    for (int cp = 0; cp < kCopies; ++cp) {
-      const int off = (wave * kCopies + cp) * 1024;
-      load_lds16(kimg + static_cast<size_t>(i) * kImg + off, &ring[slot][0][off]);
-      load_lds16(vimg + static_cast<size_t>(i) * kImg + off, &ring[slot][1][off]);
+  for (int i = 0; i < kStages - 1; ++i) copy(min(i, nb - 1), i);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s2 = 0; s2 < TR::KS; ++s2) asm volatile("" : "+v"(st[rb].q[s2]));
+
+  // Pipeline: at the top of iteration i the K operands of block i (and its
+  // V operands where registers allow, kPipeV) are in registers or on their
+  // way from LDS, and copies of blocks up to i + kStages - 2 are issued.
+  // Iteration i waits for block i + 1, passes the barrier (after which block
+  // i - 1's slot is free: its operands were read by iteration i - 1), issues
+  // the copy of block i + kStages - 1 into that slot, starts reading block
+  // i + 1's operands and computes block i.  Without kPipeV the V operands
+  // are read at the start of the block's compute and land during QK^T and
+  // the softmax.  fp32 rows of 128 (kPipeK false) read everything in place.
+  constexpr int kKRegs = 2 * TR::KS * static_cast<int>(sizeof(KOp)) / 4;
+  constexpr int kVRegs = static_cast<int>(sizeof(typename TR::VOp)) / 4;
+  constexpr int kStateRegs = RB * static_cast<int>(sizeof(ColState<T, D>)) / 4;
+  constexpr bool kPipeV = kStateRegs + 2 * (kKRegs + kVRegs) <= 180;
+  constexpr bool kPipeK = kStateRegs + 2 * kKRegs + kVRegs <= 180;
+  struct KOps { KOp k0[TR::KS], k1[TR::KS]; };
+  struct Ops {
+    KOps k;
+    typename TR::VOp vo;
+  };
+  auto read_k = [&](KOps& o, int i) {
+    const uint8_t* ki = ring[i % kStages];
+    TR::load_k_img(o.k0, ki, 0, lane);
+    TR::load_k_img(o.k1, ki, 1, lane);
+  };
+  auto read_v = [&](typename TR::VOp& vo, int i) { TR::load_v_img(vo, ring[i % kStages] + kImg, lane); };
+  // wait until block j's copies have landed in every wave; `issued` is the
+  // last block whose copies this wave has issued
+  auto wait_block = [&](int j, int issued) {
+    wait_blocks_after<kCopies, kStages - 2>(issued - j);
+    __syncthreads();
+  };
+  // Only the last block of a split can be partial: its V operands past the
+  // slab end are zeroed (pool memory there is arbitrary) and its scores
+  // masked (inside the tile).
+  auto compute = [&](const KOps& k, typename TR::VOp& vo, int i) {
+    const int valid = min(kHotBlock, t1 - t0 - kHotBlock * i);
+    if (valid < kHotBlock) {
+      int v = __builtin_amdgcn_readfirstlane(valid);
+      asm volatile("" : "+s"(v));
+      TR::mask_v(vo, v, g);
     }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) st[rb].tile(k.k0, k.k1, vo, valid, g, c);
   };
 
-  for (int i = 0; i < kPrefixStages - 1 && i < nb; ++i) copy(i);
-  for (int i = 0; i < nb; ++i) {
-    // this wave's copies of block i have landed (later blocks may still fly) ...
-    if (i + kPrefixStages - 2 < nb) wait_vmcnt<(kPrefixStages - 2) * 2 * kCopies>();
-    else wait_vmcnt<0>();
-    // ... and every wave's: block i is in LDS, block i-1's slot is free
-    __syncthreads();
-    if (i + kPrefixStages - 1 < nb) copy(i + kPrefixStages - 1);
+  if constexpr (kPipeK) {
+    auto step = [&](Ops& cur, Ops& nxt, int i) {
+      if (i + 1 < nb) {
+        wait_block(i + 1, min(nb - 1, i + kStages - 2));
+        if (i + kStages - 1 < nb) copy(i + kStages - 1, (i + kStages - 1) % kStages);
+        if (wave_active) {
+          if constexpr (!kPipeV) read_v(cur.vo, i);
+          read_k(nxt.k, i + 1);
+          if constexpr (kPipeV) read_v(nxt.vo, i + 1);
+        }
+      } else if (wave_active) {
+        if constexpr (!kPipeV) read_v(cur.vo, i);
+      }
+      if (wave_active) compute(cur.k, cur.vo, i);
+    };
+    Ops oa, ob;
+    wait_block(0, min(nb - 1, kStages - 2));
     if (wave_active) {
-      const uint8_t* ki = ring[i % kPrefixStages][0];
-      const uint8_t* vi = ring[i % kPrefixStages][1];
-      const int valid = min(kHotBlock, t1 - t0 - kHotBlock * i);
-      KOp k0[TR::KS], k1[TR::KS];
-      TR::load_k_img(k0, ki, 0, lane);
-      TR::load_k_img(k1, ki, 1, lane);
-      typename TR::VOp vo;
-      TR::load_v_img(vo, vi, lane);
-      if (valid < kHotBlock) TR::mask_v(vo, valid, g);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) st[rb].tile(k0, k1, vo, valid, g, c);
+      read_k(oa.k, 0);
+      if constexpr (kPipeV) read_v(oa.vo, 0);
+    }
+    for (int i = 0; i < nb; i += 2) {
+      step(oa, ob, i);
+      if (i + 1 >= nb) break;
+      step(ob, oa, i + 1);
+    }
+  } else {
+    for (int i = 0; i < nb; ++i) {
+      wait_block(i, min(nb - 1, i + kStages - 2));
+      if (i + kStages - 1 < nb) copy(i + kStages - 1, (i + kStages - 1) % kStages);
+      if (wave_active) {
+        Ops o;
+        read_k(o.k, i);
+        read_v(o.vo, i);
+        compute(o.k, o.vo, i);
+      }
     }
   }
 
-  if (!wave_active) return;
+  // Partial rows go out whole: each wave stages its 16 x D tile in its own
+  // part of the (now idle) ring, then writes every row as one contiguous
+  // run across the lanes (the partial stores write through the caches, so
+  // scattered pieces would cost partial-line writes).
+  __syncthreads();   // every wave is done reading the ring
+  constexpr int kStride = D + 4;   // padded row stride of the staging tile (floats)
+  static_assert(kWaves * 16 * kStride * 4 <= kStages * 2 * kImg, "staging tile exceeds the ring");
+  float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 16 * kStride;
+  if (wave_active) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float o[D / 4];
-    const float lse2 = st[rb].finish(o);
-    const int r = wrow0 + 16 * rb + n;
-    if (r < rows) {
-      const int b = a.members[cl.member_off + r / G];
-      const int h = kv_head * G + r % G;
-      const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + h;
-      store_row_slice(a.p_o + row * D + (D / 4) * g, o, D / 16);
-      if (g == 0) a.p_lse[row] = lse2;
+    for (int rb = 0; rb < RB; ++rb) {
+      float o[D / 4];
+      const float lse2 = st[rb].finish(o);
+#pragma unroll
+      for (int k = 0; k < D / 16; ++k)
+        *reinterpret_cast<f32x4*>(stage + n * kStride + (D / 4) * g + 4 * k) =
+            f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+      const int r = wrow0 + 16 * rb + n;
+      if (r < rows && g == 0) {
+        const int b = a.members[cl.member_off + mem0 + r / G];
+        const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + kv_head * G + r % G;
+        store_partial(a.p_lse + row, lse2);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int PER = D / 64;
+      for (int i = 0; i < 16; ++i) {
+        const int ri = wrow0 + 16 * rb + i;
+        if (ri >= rows) break;
+        const int b = a.members[cl.member_off + mem0 + ri / G];
+        const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + kv_head * G + ri % G;
+        float v[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[j] = stage[i * kStride + PER * lane + j];
+        if constexpr (PER % 2 == 0) {
+          store_partial_row(a.p_o + row * D + PER * lane, v, PER);
+        } else {
+#pragma unroll
+          for (int j = 0; j < PER; ++j) store_partial(a.p_o + row * D + PER * lane + j, v[j]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+
+  // this split's partials are written: publish them by counting this
+  // workgroup on the class's completion counter for its KV head
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(a.done + static_cast<size_t>(ci) * a.n_kv + kv_head, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // -------------------------------------------------------------- step kernel
-// Prefix and suffix workgroups of one decode step in one launch.  The grid
-// is a sequence of groups of 8 consecutive blocks (one per XCD); each group
-// is all-prefix or all-suffix, and the two kinds are spread evenly over the
-// sequence, so every CU runs matrix-core-heavy prefix work next to
-// memory-streaming suffix work and neither kind's tail idles the chip.  A
-// prefix block keeps blockIdx % 8 = its index % 8, i.e. its XCD.
+// Prefix and suffix workgroups of one decode step in one launch: blocks
+// [0, prefix_blocks) are prefix work (longest-running first), the rest
+// suffix work, longest slot tables first.  Workgroups are handed to the 8
+// XCDs round-robin by index and, within an XCD, to its shader engines in
+// turn, so any periodic interleave of the two kinds can pin one kind to a
+// subset of the engines; keeping each kind contiguous spreads both over all
+// CUs.  A prefix block keeps blockIdx % 8 = its index % 8, i.e. its XCD.
 template <typename T, int D>
 constexpr size_t step_smem_bytes() {
   return sizeof(PrefixSmem<T, D>) > sizeof(SuffixSmem<T, D>) ? sizeof(PrefixSmem<T, D>) : sizeof(SuffixSmem<T, D>);
@@ -685,56 +995,16 @@ template <typename T, int D, int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
-  const int groups = (a.prefix_blocks + a.suffix_blocks + kXcds - 1) / kXcds;
-  const int pgroups = a.prefix_blocks / kXcds;       // prefix_blocks is a multiple of 8
-  const int grp = blockIdx.x / kXcds, x = blockIdx.x % kXcds;
-  const int before = static_cast<int>(static_cast<int64_t>(grp) * pgroups / groups);
-  const bool is_prefix = static_cast<int>(static_cast<int64_t>(grp + 1) * pgroups / groups) > before;
-  if (is_prefix) {
-    prefix_block<T, D, RB>(a, before * kXcds + x, smem);
+  __shared__ int32_t join_flag;
+  const int blk = blockIdx.x;
+  if (blk < a.prefix_blocks) {
+    prefix_block<T, D, RB>(a, blk, smem);
   } else {
-    const int sb = (grp - before) * kXcds + x;
-    if (sb < a.suffix_blocks) suffix_block<T, D>(a, sb, smem);
+    const int sb = blk - a.prefix_blocks;
+    if (sb < a.suffix_blocks) suffix_block<T, D>(a, sb, smem, join_flag);
   }
 }
 
-// ------------------------------------------------------------- merge kernel
-// One wave per (request, query head): joins the request's prefix splits and
-// suffix-part partials.  Requests finished by their suffix block (no HOT
-// prefix, one part) return at once.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(StepArgs a) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int idx = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (idx >= a.batch * a.n_q) return;
-  const int b = idx / a.n_q, h = idx % a.n_q;
-  const int r = a.rank_of[b];
-  const int c0 = a.part_start[r];
-  const int nparts = a.part_start[r + 1] - c0;
-  const int cls = a.req_class[b];
-  if (cls < 0 && nparts == 1) return;
-  const int ns = cls >= 0 ? a.classes[cls].n_splits : 0;
-  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
-  float acc[PER];
-  const float l2 = join_parts<PER, 32>(
-      ns + nparts, lane,
-      [&](int p) {
-        return p < ns ? a.p_lse[prow0 + static_cast<size_t>(p) * a.n_q]
-                      : a.s_lse[static_cast<size_t>(c0 + p - ns) * a.n_q + h];
-      },
-      [&](int p) -> const float* {
-        return p < ns ? a.p_o + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
-                      : a.s_o + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane;
-      },
-      acc);
-  T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + PER * lane;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
-  if (lane == 0) a.lse[idx] = l2 * 0.69314718055994531f;
-}
-
-// ------------------------------------------------------------ append kernel
 __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, const u32x4* v_new,
                                                           const int32_t* slots, int32_t n,
                                                           u32x4* k_cold, u32x4* v_cold,
@@ -752,27 +1022,36 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, co
 
 template <typename T, int D>
 hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
-  if (ev) (void)hipEventRecord(ev[0], stream);
-  const int blocks = ((a.prefix_blocks + a.suffix_blocks + kXcds - 1) / kXcds) * kXcds;
+  // With timing events, the kernel is launched through hipExtLaunchKernelGGL,
+  // which stamps the events with the kernel's own start and end.
+  hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+  const int blocks = a.prefix_blocks + a.suffix_blocks;
   if (backend == 2) {
     if constexpr (sizeof(T) == 2) {
-      step_kernel<T, D, kDenseRB><<<blocks, kThreads, 0, stream>>>(a);
+      hipExtLaunchKernelGGL(step_kernel<T, D, kDenseRB>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    step_kernel<T, D, kCascadeRB><<<blocks, kThreads, 0, stream>>>(a);
+    hipExtLaunchKernelGGL(step_kernel<T, D, kCascadeRB>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
   }
-  if (ev) (void)hipEventRecord(ev[1], stream);
-  if (a.need_merge) {
-    const int pairs = a.batch * a.n_q;
-    merge_kernel<T, D><<<(pairs + kWaves - 1) / kWaves, kThreads, 0, stream>>>(a);
-  }
-  if (ev) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int grid = static_cast<int>(std::min<size_t>((n + kThreads - 1) / kThreads, 1024));
+  zero_kernel<<<grid, kThreads, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_t* slots, int32_t n,
                               void* k_cold, void* v_cold, int64_t row_bytes, int32_t cold_cap,

@@ -121,11 +121,14 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   // work (KV heads x M-tiles x tokens) spreads over about kTargetBlocks
   // workgroups, with at least kMinSplitTokens tokens per split.
   const int32_t rb = backend == GKV_BACKEND_DENSE ? kDenseRB : kCascadeRB;
-  const int32_t m_tile = 64 * rb;
+  const int32_t tm = tile_members(group, rb);
+  if (tm < 1) {
+    err = "query group of " + std::to_string(group) + " heads exceeds one prefix tile";
+    return -1;
+  }
   int64_t units = 0;
   for (int32_t c = 0; c < n_classes; ++c)
-    units += static_cast<int64_t>(n_kv) * ceil_div(static_cast<int64_t>(class_size[c]) * group, m_tile) *
-             a.classes[c].len;
+    units += static_cast<int64_t>(n_kv) * ceil_div(class_size[c], tm) * a.classes[c].len;
   const int64_t split_tokens = std::max<int64_t>(
       kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), kTargetBlocks), kPrefixTile));
   int32_t max_splits = 0;
@@ -138,11 +141,11 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     s = ceil_div(len, chunk);
     cd.n_splits = static_cast<int32_t>(s);
     cd.chunk = static_cast<int32_t>(chunk);
-    cd.m_tiles = static_cast<int32_t>(ceil_div(static_cast<int64_t>(cd.n_members) * group, m_tile));
+    cd.m_tiles = static_cast<int32_t>(ceil_div(cd.n_members, tm));
     cd.n_groups = n_kv * cd.n_splits;
     cd.block_base = blocks;
     cd.n_blocks = kXcds * static_cast<int32_t>(ceil_div(cd.n_groups, kXcds)) * cd.m_tiles;
-    cd.pad_ = 0;
+    cd.done_target = 0;   // set by the caller from its running totals
     blocks += cd.n_blocks;
     max_splits = std::max(max_splits, cd.n_splits);
   }

@@ -28,7 +28,7 @@ struct Plan {
   int32_t prefix_blocks = 0;    // prefix workgroups (including idle XCD padding)
   int32_t suffix_blocks = 0;    // suffix workgroups
   int32_t n_parts = 0;          // suffix parts (>= one per request)
-  int32_t multi_part = 0;       // some request needs the merge kernel
+  int32_t multi_part = 0;       // some request's output is joined from several partials
   int64_t prefix_rows = 0;      // prefix partial rows (B * max_splits * n_q)
   int64_t suffix_rows = 0;      // suffix partial rows
 };

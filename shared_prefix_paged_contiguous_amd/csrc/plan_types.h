@@ -1,16 +1,18 @@
 // Work description of one decode step, shared by the host planner and the
 // device kernels.  The whole description travels in the kernel arguments
-// (about 9 KB), so a step needs no host-to-device copy before its kernels.
+// (about 15 KB), so a step needs no host-to-device copy before its kernels.
 #pragma once
 
 #include <cstdint>
 
 namespace gkv {
 
-// Prefix kernel tiling.  A workgroup is 4 waves; each wave owns RB blocks of
-// 16 query rows (one MFMA column block each), so a workgroup tile covers
-// 64*RB rows of one class and one KV head.  K/V tiles of kPrefixTile tokens
-// are staged through LDS.
+// Step kernel tiling.  A workgroup is 4 waves (one per SIMD); two
+// workgroups share a CU, each with its own barriers, so one's MFMA and
+// softmax work overlaps the other's waits.  In a prefix workgroup each wave
+// owns RB blocks of 16 query rows (one MFMA column block each), so a
+// workgroup tile covers 64*RB rows of one class and one KV head and every
+// HOT block it streams through LDS feeds all of them.
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefixTile = 64;
@@ -21,8 +23,12 @@ constexpr int kWaveTokens = 1024; // most slot-table tokens one suffix wave cove
 constexpr int kSuffixPart = kWaves * kWaveTokens;   // tokens per suffix workgroup
 constexpr int kMaxSplits = 64;    // L splits per prefix class
 constexpr int kHotBlock = 32;     // tokens per HOT block; slabs start on block boundaries
-constexpr int kPrefixStages = 4;  // LDS ring depth of the prefix kernel (blocks in flight + 1)
+constexpr int kRingBytes = 64 * 1024;   // LDS ring of a prefix workgroup (K+V images of 3..8 blocks)
 constexpr int kXcds = 8;          // MI355X: workgroups go to the 8 XCDs round-robin
+
+// Requests per prefix M-tile: a tile holds whole requests (all G query
+// heads of a member for the tile's KV head), at most 64 * RB rows.
+constexpr int tile_members(int group, int rb) { return kWaves * 16 * rb / group; }
 
 // Limits of one step (the description must fit the kernel arguments).
 constexpr int kMaxBatch = 1024;
@@ -40,11 +46,11 @@ struct ClassDesc {
   int32_t member_off;   // first entry in members[]
   int32_t n_splits;     // L splits S_c
   int32_t chunk;        // tokens per split (the last split may be shorter)
-  int32_t m_tiles;      // ceil(n_members * G / (64 * RB))
+  int32_t m_tiles;      // ceil(n_members / tile_members(G, RB)): M-tiles hold whole requests
   int32_t n_groups;     // n_kv * n_splits
   int32_t block_base;   // first prefix block
   int32_t n_blocks;     // 8 * ceil(n_groups / 8) * m_tiles
-  int32_t pad_;
+  uint32_t done_target; // value of the class's completion counters once this step's splits are in
 };
 
 // Suffix work: one workgroup per (suffix part, KV head).  Requests are
@@ -53,8 +59,13 @@ struct ClassDesc {
 // part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
 // and the 4 waves take consecutive quarters of it.  Block i -> part
 // i / n_kv, KV head i % n_kv.  A request with no HOT prefix and one part is
-// finished in the suffix workgroup's epilogue; otherwise each part writes a
-// partial and the merge kernel joins them with the request's prefix splits.
+// finished in the suffix workgroup's epilogue.  Otherwise every prefix split
+// and suffix part writes a partial per (request, query head).  A prefix
+// workgroup then bumps its class's completion counter for its KV head; the
+// suffix part of (request, KV head) that arrives last among the request's
+// parts waits until that counter reaches done_target and joins the partials
+// into the output (no separate merge pass).  Prefix workgroups precede all
+// suffix workgroups in the grid and wait on nothing, so the wait ends.
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
@@ -63,7 +74,7 @@ struct StepArgs {
   int32_t suffix_blocks;       // n_parts * n_kv
   int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
   int32_t multi_part;          // some request has more than one suffix part
-  int32_t need_merge;          // some request has a HOT prefix or several parts
+  int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
   const void* q;
   void* out;
   float* lse;
@@ -79,6 +90,8 @@ struct StepArgs {
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
   float* s_o;                  // suffix-part partials, row = part * n_q + h
   float* s_lse;
+  int32_t* counters;           // [kMaxBatch][n_kv] suffix-part arrivals (zero between calls)
+  uint32_t* done;              // [kMaxClasses][n_kv] prefix-workgroup completions (running totals)
   ClassDesc classes[kMaxClasses];
   int32_t indptr[kMaxBatch + 1];        // slot-table row pointers (host copy of cold_indptr)
   int32_t part_start[kMaxBatch + 1];    // by rank

@@ -250,6 +250,37 @@ def test_repeated_calls_identical_and_failed_call_writes_nothing():
     assert bool((sentinel == 7.0).all())
 
 
+def test_join_counters_survive_rebinds_and_batch_changes():
+    """The step kernel coordinates its partial joins through counters in the
+    workspace.  A freshly bound workspace full of garbage is cleared by the
+    first call; later calls (same batch, a smaller batch, a rebind to a
+    second garbage workspace) must all stay exact."""
+    s = spec(batch=6, prefix_len=700, hot_capacity=1024, cold_capacity=30000,
+             fixed_suffix=(5000, 3, 0, 4100, 17, 9000))
+    w = workloads.make(s)
+    st = DecodeState(w)
+    ref_o, ref_l = oracle_ref(w)
+    for fill in (0xFF, 0x7F):
+        ws = torch.full_like(st.workspace, fill)
+        st.ctx.bind_workspace(ws)
+        st.workspace = ws
+        for _ in range(2):
+            out, lse = st.new_outputs()
+            st.run(out, lse)
+            torch.cuda.synchronize()
+            check(out, lse, ref_o, ref_l)
+        # the first three requests alone (indptr prefix of the same tables)
+        out3, lse3 = st.new_outputs()
+        st.ctx.attn_decode(0, st.q[:3], st.hot_ids[:3], st.indptr_h[:4], st.indptr_d[:4], st.indices_d,
+                           out3[:3], lse3[:3])
+        torch.cuda.synchronize()
+        check(out3, lse3, ref_o, ref_l, requests=[0, 1, 2])
+    out, lse = st.new_outputs()
+    st.run(out, lse)
+    torch.cuda.synchronize()
+    check(out, lse, ref_o, ref_l)
+
+
 def test_dispatch_follows_m_eff():
     s = spec(batch=16, n_q=32, n_kv=8, fixed_suffix=tuple([8] * 16))
     w = workloads.make(s)
@@ -291,12 +322,12 @@ def test_full_size_sampled_requests(name):
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_long_suffixes_span_several_parts(force):
     """Slot tables longer than one suffix workgroup's share (4096 tokens) are
-    split into parts joined by the merge kernel; mixed with single-part
+    split into parts joined inside the step kernel; mixed with single-part
     requests and a prefix-only request."""
     s = spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
              fixed_suffix=(5000, 10, 0, 9000))
     w = workloads.make(s)
     st, out, lse, _ = run(w, force=force)
     plan = st.ctx.last_plan()
-    assert plan["merge_kernel"] == 1 and plan["n_suffix_parts"] == 2 + 1 + 1 + 3
+    assert plan["joins_partials"] == 1 and plan["n_suffix_parts"] == 2 + 1 + 1 + 3
     check(out, lse, *oracle_ref(w))
