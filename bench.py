@@ -81,6 +81,37 @@ def estimate_step_bytes(w):
     return 2 * tokens * s.n_kv * s.head_dim * e
 
 
+KERNEL_SOURCES = ("kernels.hip", "kernels.h", "plan_types.h")
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the device-code sources: identifies the kernels a set of
+    hardware counters was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "shared_prefix_paged_contiguous_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per step-kernel launch from the committed rocprofv3 summary
+    of this workload (calibrated FETCH_SIZE + WRITE_SIZE), or None when the
+    summary is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"step_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("counters:"):
+                kv = dict(x.split("=", 1) for x in line.split()[1:])
+                if kv.get("kernel_sha") != kernel_source_sha():
+                    return None
+                return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 def cpu_baseline(w, target_s: float):
     """The float64 oracle, unmodified, on a bounded sample of requests."""
     import torch
@@ -94,9 +125,11 @@ def cpu_baseline(w, target_s: float):
     pk = [f64(x) for x in w.prefix_k]
     pv = [f64(x) for x in w.prefix_v]
     q = f64(w.q)
-    done, t_used = [], 0.0
-    t_all = time.perf_counter()
-    for b in range(w.batch):
+    # requests of the workload in order, cycling through the batch again
+    # until about target_s seconds of oracle work are done
+    done, t_used = 0, 0.0
+    while t_used < target_s:
+        b = done % w.batch
         sk, sv = w.suffix_rows(b)
         sks = [None] * w.batch
         svs = [None] * w.batch
@@ -104,15 +137,13 @@ def cpu_baseline(w, target_s: float):
         t = time.perf_counter()
         decode_step(q, pk, pv, w.request_prefix, sks, svs, requests=[b])
         t_used += time.perf_counter() - t
-        done.append(b)
-        if time.perf_counter() - t_all >= target_s:
-            break
+        done += 1
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": len(done) / t_used, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} requests of the same workload (all {w.spec.n_q} query "
-                      f"heads each), float64 numpy; BLAS threads={threads}, host cpus={os.cpu_count()}; "
-                      f"{t_used:.1f} s of oracle time"}
+    return {"value": done / t_used, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} request decodes ({done / w.batch:.1f} passes over the {w.batch} requests of the "
+                      f"same workload, all {w.spec.n_q} query heads each), float64 numpy; BLAS "
+                      f"threads={threads}, host cpus={os.cpu_count()}; {t_used:.1f} s of oracle time"}
 
 
 def build_state(w, replicas, force):
@@ -187,13 +218,15 @@ def run_bench(args):
         f"backend={binding.BACKEND_NAMES[backend]}, host plan {plan['host_plan_us']:.2f} us")
 
     # same-layer ("warm", cache-resident) timing, reported for contrast only
-    e0.record(stream)
-    for i in range(args.steps):
-        ctx.cold_append(0, k_new, v_new, slots_new, stream=stream)
-        st.run(out, lse, layer=0, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_warm = e0.elapsed_time(e1) / args.steps
+    ms_warm = None
+    if not args.no_warm:
+        e0.record(stream)
+        for i in range(args.steps):
+            ctx.cold_append(0, k_new, v_new, slots_new, stream=stream)
+            st.run(out, lse, layer=0, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_warm = e0.elapsed_time(e1) / args.steps
 
     # per-kernel durations with HIP events recorded by the library on this stream
     ctx.kernel_timing(args.steps)
@@ -208,7 +241,8 @@ def run_bench(args):
     dom_bytes = alg["kernel_bytes"][dom]
     achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": dom + "_kernel",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": counter_traffic(s.name),
+                "kernel": dom + "_kernel",
                 "kernel_us": round(kern_ms[dom] * 1e3, 2), "kernel_bytes": dom_bytes}
     if alg["prefix_flops"] > 0:
         roofline["step_kernel_mfma_frac"] = round((alg["prefix_flops"] + alg["suffix_flops"]) /
@@ -228,7 +262,7 @@ def run_bench(args):
         "achieved_hbm_gbps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": alg["step_bytes"],
-        "warm_ms_per_step": round(ms_warm, 5),
+        "warm_ms_per_step": round(ms_warm, 5) if ms_warm is not None else None,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
         "kernel_note": "step = the one kernel of attn_decode: prefix splits, suffix parts and their join",
         "host_plan_us": round(plan["host_plan_us"], 3),
@@ -293,6 +327,8 @@ def main():
     ap.add_argument("--backend", default="auto", choices=["auto", "cascade", "dense"])
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the same-layer pass (profiling: every step kernel then reads from HBM)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
