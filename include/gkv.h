@@ -212,11 +212,11 @@ typedef struct {
   int32_t m_eff;              /* B * n_q / n_kv of the step */
   int32_t n_classes;          /* distinct HOT prefixes in the step */
   int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
-  int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV heads) */
+  int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV-head groups) */
   int32_t n_suffix_parts;     /* slot-table parts (>= one per request) */
   int32_t joins_partials;     /* 1 if some output is joined from several partials (a HOT
                                  prefix or a multi-part slot table), inside the step kernel */
-  int32_t pad_;
+  int32_t suffix_part_tokens; /* slot-table tokens per suffix part this step */
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
 } gkv_plan_info;

@@ -56,7 +56,7 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [("backend", ctypes.c_int32), ("m_eff", ctypes.c_int32),
                 ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
-                ("joins_partials", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("joins_partials", ctypes.c_int32), ("suffix_part_tokens", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
 
 

@@ -42,7 +42,6 @@ struct gkv_ctx {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   bool ws_clear = false;    // counters of a newly bound workspace still to be zeroed
-  uint32_t done_total[gkv::kMaxClasses] = {};   // completion counter totals per class slot
   int32_t m_sat;
   int32_t force;
   std::string err;
@@ -73,23 +72,17 @@ int device_fail(gkv_ctx* ctx, const char* what, hipError_t e) {
   return fail(ctx, GKV_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Counters of the in-kernel join at the start of the workspace: suffix-part
-// arrivals per (request, KV head), which every step leaves at zero, then
-// prefix-split completions per (class slot, KV head), running totals whose
-// per-step targets the host tracks.  Zeroed by the first step on a newly
-// bound workspace.
-size_t part_counter_bytes(const gkv_config& c) {
-  return gkv::align256(static_cast<size_t>(gkv::kMaxBatch) * c.n_kv_heads * sizeof(int32_t));
-}
+// Arrival counters of the in-kernel join, one per (request, KV head), at the
+// start of the workspace.  Zeroed by the first step on a newly bound
+// workspace; every step leaves them zero again (the join resets its counter).
 size_t counter_bytes(const gkv_config& c) {
-  return part_counter_bytes(c) +
-         gkv::align256(static_cast<size_t>(gkv::kMaxClasses) * c.n_kv_heads * sizeof(int32_t));
+  return gkv::align256(static_cast<size_t>(gkv::kMaxBatch) * c.n_kv_heads * sizeof(int32_t));
 }
 
 size_t elem_size(const gkv_config& c) { return c.dtype == GKV_BF16 ? 2 : 4; }
 
 gkv::PlanShape shape_of(const gkv_config& c) {
-  return gkv::PlanShape{c.n_q_heads, c.n_kv_heads, c.head_dim};
+  return gkv::PlanShape{c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype == GKV_BF16};
 }
 
 int check_layer(gkv_ctx* ctx, int32_t layer) {
@@ -187,7 +180,7 @@ int gkv_hot_write(gkv_ctx* ctx, int32_t layer, int32_t prefix_id, int32_t token_
 int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix_tokens, size_t* bytes) {
   if (!ctx || !bytes || max_batch < 1 || max_suffix_tokens < 0) return GKV_ERR_INVALID;
   const gkv::PlanShape s = shape_of(ctx->cfg);
-  const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * 4;
+  const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * elem_size(ctx->cfg);   // partial rows: input dtype
   const int64_t pr = gkv::prefix_rows_bound(s, max_batch);
   const int64_t sr = gkv::suffix_rows_bound(s, max_batch, max_suffix_tokens);
   *bytes = counter_bytes(ctx->cfg) + gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
@@ -372,7 +365,7 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
     return fail(ctx, GKV_ERR_INVALID, err);
 
   // workspace: [counters][prefix o][prefix lse][suffix o][suffix lse]
-  const size_t row = static_cast<size_t>(c.head_dim) * 4;
+  const size_t row = static_cast<size_t>(c.head_dim) * elem_size(c);   // partial rows: input dtype
   const size_t off_po = counter_bytes(c);
   const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
   const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
@@ -402,10 +395,9 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
   a.cold_indices = cold_indices_d;
   a.counters = reinterpret_cast<int32_t*>(ws);
-  a.done = reinterpret_cast<uint32_t*>(ws + part_counter_bytes(c));
-  a.p_o = reinterpret_cast<float*>(ws + off_po);
+  a.p_o = ws + off_po;
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
-  a.s_o = reinterpret_cast<float*>(ws + off_so);
+  a.s_o = ws + off_so;
   a.s_lse = reinterpret_cast<float*>(ws + off_sl);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -418,15 +410,8 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
     if ((e = gkv::launch_zero_i32(a.counters, counter_bytes(c) / 4, st)) != hipSuccess)
       return device_fail(ctx, "counter clear launch", e);
     ctx->ws_clear = false;
-    for (uint32_t& t : ctx->done_total) t = 0;
   }
-  // every (class slot, KV head) counter gains one count per prefix workgroup
-  // of the class and head: n_splits * m_tiles
-  for (int32_t ci = 0; ci < a.n_classes; ++ci)
-    a.classes[ci].done_target = ctx->done_total[ci] +
-                                static_cast<uint32_t>(a.classes[ci].n_splits) * static_cast<uint32_t>(a.classes[ci].m_tiles);
   if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);
-  for (int32_t ci = 0; ci < a.n_classes; ++ci) ctx->done_total[ci] = a.classes[ci].done_target;
 
   ctx->last.backend = backend;
   ctx->last.m_eff = plan.m_eff;
@@ -435,6 +420,7 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   ctx->last.n_suffix_blocks = plan.suffix_blocks;
   ctx->last.n_suffix_parts = plan.n_parts;
   ctx->last.joins_partials = plan.multi_part;
+  ctx->last.suffix_part_tokens = plan.part_tokens;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->have_last = true;

@@ -309,6 +309,58 @@ struct ColState {
   }
 };
 
+// One 32-token tile for RB row blocks that share the K/V operands, in
+// phases: all QK^T products, then all softmax updates, then all PV
+// products.  The row blocks' dependency chains are independent, so each
+// phase's work for one row block overlaps the latency of another's.  Same
+// arithmetic, per row block, as ColState::tile.
+template <typename T, int D, int RB>
+__device__ __forceinline__ void tile_rows(ColState<T, D> (&st)[RB], const typename Traits<T, D>::KOp (&k0)[Traits<T, D>::KS],
+                                          const typename Traits<T, D>::KOp (&k1)[Traits<T, D>::KS],
+                                          const typename Traits<T, D>::VOp& vo, int valid, int g, float c) {
+  using TR = Traits<T, D>;
+  f32x4 s0[RB], s1[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    s0[rb] = TR::qk(k0, st[rb].q);
+    s1[rb] = TR::qk(k1, st[rb].q);
+  }
+  if (valid < 32) {
+    int v = __builtin_amdgcn_readfirstlane(valid);
+    asm volatile("" : "+s"(v));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * g + i >= v) s0[rb][i] = kNegInf;
+        if (16 + 4 * g + i >= v) s1[rb][i] = kNegInf;
+      }
+  }
+  f32x4 p0[RB], p1[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    ColState<T, D>& cs = st[rb];
+    const float lmx = fmaxf(fmaxf(fmaxf(s0[rb][0], s0[rb][1]), fmaxf(s0[rb][2], s0[rb][3])),
+                            fmaxf(fmaxf(s1[rb][0], s1[rb][1]), fmaxf(s1[rb][2], s1[rb][3]))) * c;
+    if (__any(lmx > cs.m + kLazy)) {
+      const float m_new = fmaxf(cs.m, wave_max_groups(lmx));
+      const float alpha = __builtin_amdgcn_exp2f(cs.m - m_new);
+      cs.l *= alpha;
+#pragma unroll
+      for (int j = 0; j < TR::EPB; ++j) cs.acc[j] *= alpha;
+      cs.m = m_new;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[rb][i], c, -cs.m));
+      p1[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[rb][i], c, -cs.m));
+    }
+    cs.l += (p0[rb][0] + p0[rb][1]) + (p0[rb][2] + p0[rb][3]) + (p1[rb][0] + p1[rb][1]) + (p1[rb][2] + p1[rb][3]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
+}
+
 // Partials cross workgroups (and XCDs, whose L2 caches are not coherent
 // with one another) inside one launch, so they are written and read with
 // agent-scope relaxed atomic accesses: these bypass the non-coherent cache
@@ -340,6 +392,47 @@ __device__ __forceinline__ void load_partial_row(const float* src, float (&v)[PE
     for (int j = 0; j < PER; ++j) v[j] = load_partial(src + j);
   }
 }
+// PER consecutive values of a partial row in the input dtype T (PER even
+// or T = float): 32-bit (two bf16) or 64-bit (two fp32) agent-scope accesses
+template <typename T, int PER>
+__device__ __forceinline__ void store_partial_vals(T* dst, const float (&v)[PER]) {
+  if constexpr (sizeof(T) == 2 && PER == 1) {
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(dst), __builtin_bit_cast(uint16_t, static_cast<__bf16>(v[0])),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if constexpr (sizeof(T) == 2) {
+    static_assert(PER % 2 == 0, "bf16 partial slices: one or an even number");
+#pragma unroll
+    for (int k = 0; k < PER; k += 2) {
+      const uint32_t w = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[k]))) |
+                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v[k + 1]))) << 16);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(dst + k), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else if constexpr (PER % 2 == 0) {
+    store_partial_row(reinterpret_cast<float*>(dst), v, PER);
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) store_partial(reinterpret_cast<float*>(dst) + k, v[k]);
+  }
+}
+template <typename T, int PER>
+__device__ __forceinline__ void load_partial_vals(const T* src, float (&v)[PER]) {
+  if constexpr (sizeof(T) == 2 && PER == 1) {
+    const uint16_t w = __hip_atomic_load(reinterpret_cast<const uint16_t*>(src), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    v[0] = static_cast<float>(__builtin_bit_cast(__bf16, w));
+  } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < PER; k += 2) {
+      const uint32_t w = __hip_atomic_load(reinterpret_cast<const uint32_t*>(src + k), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      v[k] = static_cast<float>(__builtin_bit_cast(__bf16, static_cast<uint16_t>(w)));
+      v[k + 1] = static_cast<float>(__builtin_bit_cast(__bf16, static_cast<uint16_t>(w >> 16)));
+    }
+  } else {
+    load_partial_row<PER>(reinterpret_cast<const float*>(src), v);
+  }
+}
+
 // all of this wave's partial stores have completed
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -419,9 +512,11 @@ __device__ __forceinline__ void join_row(const StepArgs& a, int b, int h, int la
                                    : a.s_lse + static_cast<size_t>(c0 + p - ns) * a.n_q + h);
       },
       [&](int p, float (&v)[PER]) {
-        load_partial_row<PER>(p < ns ? a.p_o + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
-                                     : a.s_o + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane,
-                              v);
+        const T* po = static_cast<const T*>(a.p_o);
+        const T* so = static_cast<const T*>(a.s_o);
+        load_partial_vals<T, PER>(p < ns ? po + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
+                                         : so + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane,
+                                  v);
       },
       acc);
   T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + PER * lane;
@@ -430,40 +525,40 @@ __device__ __forceinline__ void join_row(const StepArgs& a, int b, int h, int la
   if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + h] = l2 * 0.69314718055994531f;
 }
 
-// Counts the arrival of one of request b's suffix parts for KV head g; true
-// for the part that completes the set, which also rewinds the counter to
-// zero for the next call.  Protocol: every wave of the arriving workgroup
-// has stored its partial rows with agent-scope accesses and waited for them
-// to complete, then the workgroup barrier; the arrival is an agent-scope
-// read-modify-write whose result the workgroup waits for, so the workgroup
-// that sees the last count issues its agent-scope partial loads only after
-// every contributor's partials are in place.
-__device__ __forceinline__ bool arrive(const StepArgs& a, int b, int g, int n_parts) {
-  int32_t* cnt = a.counters + static_cast<size_t>(b) * a.n_kv + g;
-  const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool last = old == n_parts - 1;
-  if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return last;
+// Number of partials request b's output is joined from, per KV head: its
+// class's prefix splits and its suffix parts.
+__device__ __forceinline__ int partials_of(const StepArgs& a, int b) {
+  const int r = a.rank_of[b];
+  const int cls = a.req_class[b];
+  return (cls >= 0 ? a.classes[cls].n_splits : 0) + a.part_start[r + 1] - a.part_start[r];
 }
 
-// Most polls of a completion counter before a wait gives up.  A poll is an
+// Counts the arrival of one partial of (request b, KV head g).  Protocol:
+// every wave of the arriving workgroup has stored its partial rows with
+// agent-scope accesses and waited for them to complete, then the workgroup
+// barrier; only then is the arrival counted, so a count seen by the join
+// workgroup means the partial is in place.
+__device__ __forceinline__ void arrive(const StepArgs& a, int b, int g) {
+  __hip_atomic_fetch_add(a.counters + static_cast<size_t>(b) * a.n_kv + g, 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Most polls of an arrival counter before a join gives up.  A poll is an
 // agent-scope load plus a short sleep (about a microsecond), so the bound
 // (~0.1 s) is far beyond any step's duration; it only guarantees that the
-// kernel ends even if the counter were never to arrive (the join then reads
+// kernel ends even if a count were never to arrive (the join then reads
 // whatever the partials hold).
 constexpr int kSpinLimit = 1 << 16;
 
-// Waits until every prefix workgroup of class cls and KV head g has
-// published its partials (the class's completion counter reaches its
-// target; the counter is a wrapping running total).  One thread calls it.
-__device__ __forceinline__ void wait_prefix_done(const StepArgs& a, int cls, int g) {
-  const uint32_t* d = a.done + static_cast<size_t>(cls) * a.n_kv + g;
-  const uint32_t target = a.classes[cls].done_target;
+// Waits until all n partials of (request b, KV head g) have arrived, then
+// rewinds the counter to zero for the next call.  One thread calls it.
+__device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, int n) {
+  int32_t* cnt = a.counters + static_cast<size_t>(b) * a.n_kv + g;
   for (int it = 0; it < kSpinLimit; ++it) {
-    const uint32_t v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (static_cast<int32_t>(v - target) >= 0) break;
+    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
     __builtin_amdgcn_s_sleep(1);
   }
+  __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ suffix blocks
@@ -480,7 +575,7 @@ struct SuffixSmem {
 };
 
 template <typename T, int D>
-__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw, int32_t& join_flag) {
+__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
@@ -493,6 +588,7 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int part = blk / a.n_kv;
   const int gk = blk - part * a.n_kv;
+  if (part >= a.part_start[a.batch]) return;   // grid padding
   int lo = 0, hi = a.batch - 1;     // rank: last r with part_start[r] <= part
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -554,26 +650,15 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       st.tile(k0, k1, vo, min(kSuffixTile, len - kSuffixTile * i), g, c);
     };
 
-    if constexpr (sizeof(T) * D <= 256) {
-      // two register sets, alternating: tile i+1 loads while tile i computes
-      KOp ka0[TR::KS], ka1[TR::KS], kb0[TR::KS], kb1[TR::KS];
-      VVec va[8], vb[8];
-      load_kv(0, ka0, ka1, va);
-      for (int i = 0; i < n_tiles; i += 2) {
-        if (i + 1 < n_tiles) load_kv(i + 1, kb0, kb1, vb);
-        run_tile(ka0, ka1, va, i);
-        if (i + 1 >= n_tiles) break;
-        if (i + 2 < n_tiles) load_kv(i + 2, ka0, ka1, va);
-        run_tile(kb0, kb1, vb, i + 1);
-      }
-    } else {
-      // fp32 rows of 128: two sets would not fit the register file
-      KOp k0[TR::KS], k1[TR::KS];
-      VVec v[8];
-      for (int i = 0; i < n_tiles; ++i) {
-        load_kv(i, k0, k1, v);
-        run_tile(k0, k1, v, i);
-      }
+    // one tile at a time: the loads of a tile are in flight only while
+    // the wave waits for them, and the other waves of the CU fill the time
+    // (measured: two alternating register sets gained nothing and cost 64
+    // registers)
+    KOp k0[TR::KS], k1[TR::KS];
+    VVec v[8];
+    for (int i = 0; i < n_tiles; ++i) {
+      load_kv(i, k0, k1, v);
+      run_tile(k0, k1, v, i);
     }
     lse2 = st.finish(o);
   }
@@ -607,32 +692,16 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
     } else {
       const size_t row = static_cast<size_t>(part) * a.n_q + hc;
-      if constexpr (PER % 2 == 0) {
-        store_partial_row(a.s_o + row * D + PER * lane, acc, PER);
-      } else {
-#pragma unroll
-        for (int k = 0; k < PER; ++k) store_partial(a.s_o + row * D + PER * lane + k, acc[k]);
-      }
+      store_partial_vals<T, PER>(static_cast<T*>(a.s_o) + row * D + PER * lane, acc);
       if (lane == 0) store_partial(a.s_lse + row, l2);
     }
   }
   if (final_here) return;
 
-  // This part's partial is written.  The last of the request's parts to
-  // arrive (for this KV head) waits for the request's prefix splits, if
-  // any, and joins all partials.
+  // this part's partial is written: count it for the request's join
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int n_parts = a.part_start[lo + 1] - a.part_start[lo];
-    const bool go = n_parts == 1 || arrive(a, b, gk, n_parts);
-    const int cls = a.req_class[b];
-    if (go && cls >= 0) wait_prefix_done(a, cls, gk);
-    join_flag = go ? 1 : 0;
-  }
-  __syncthreads();
-  if (join_flag == 0) return;
-  for (int col = wave; col < G; col += kWaves) join_row<T, D>(a, b, gk * G + col, lane);
+  if (threadIdx.x == 0) arrive(a, b, gk);
 }
 
 // ------------------------------------------------------------ prefix kernel
@@ -878,8 +947,7 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       asm volatile("" : "+s"(v));
       TR::mask_v(vo, v, g);
     }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) st[rb].tile(k.k0, k.k1, vo, valid, g, c);
+    tile_rows<T, D, RB>(st, k.k0, k.k1, vo, valid, g, c);
   };
 
   if constexpr (kPipeK) {
@@ -929,6 +997,15 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   constexpr int kStride = D + 4;   // padded row stride of the staging tile (floats)
   static_assert(kWaves * 16 * kStride * 4 <= kStages * 2 * kImg, "staging tile exceeds the ring");
   float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 16 * kStride;
+  // the tile's request ids, one per lane (tile_members <= 128): rows then
+  // find theirs with a lane read instead of a dependent load per row
+  const int mb0 = lane < n_mem ? a.members[cl.member_off + mem0 + lane] : 0;
+  const int mb1 = lane + 64 < n_mem ? a.members[cl.member_off + mem0 + 64 + lane] : 0;
+  auto member_of_row = [&](int ri) {   // ri wave-uniform
+    const int k = ri / G;
+    return k < 64 ? __builtin_amdgcn_readlane(mb0, k) : __builtin_amdgcn_readlane(mb1, k - 64);
+  };
+  static_assert(kWaves * 16 * 2 <= 128, "tile members exceed two lanes' worth");
   if (wave_active) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -938,11 +1015,15 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       for (int k = 0; k < D / 16; ++k)
         *reinterpret_cast<f32x4*>(stage + n * kStride + (D / 4) * g + 4 * k) =
             f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-      const int r = wrow0 + 16 * rb + n;
-      if (r < rows && g == 0) {
-        const int b = a.members[cl.member_off + mem0 + r / G];
-        const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + kv_head * G + r % G;
-        store_partial(a.p_lse + row, lse2);
+      // lse of row n: move it to lane n, then lanes < 16 store
+      const float lse_n = __shfl(lse2, n);
+      const int r = wrow0 + 16 * rb + lane;
+      const int kr = r / G;
+      const int bl0 = __shfl(mb0, kr % 64), bl1 = __shfl(mb1, kr % 64);
+      const int bl = kr < 64 ? bl0 : bl1;
+      if (lane < 16 && r < rows) {
+        const size_t row = (static_cast<size_t>(bl) * a.max_splits + split) * a.n_q + kv_head * G + r % G;
+        store_partial(a.p_lse + row, lse_n);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -951,17 +1032,12 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       for (int i = 0; i < 16; ++i) {
         const int ri = wrow0 + 16 * rb + i;
         if (ri >= rows) break;
-        const int b = a.members[cl.member_off + mem0 + ri / G];
+        const int b = member_of_row(ri);
         const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + kv_head * G + ri % G;
         float v[PER];
 #pragma unroll
         for (int j = 0; j < PER; ++j) v[j] = stage[i * kStride + PER * lane + j];
-        if constexpr (PER % 2 == 0) {
-          store_partial_row(a.p_o + row * D + PER * lane, v, PER);
-        } else {
-#pragma unroll
-          for (int j = 0; j < PER; ++j) store_partial(a.p_o + row * D + PER * lane + j, v[j]);
-        }
+        store_partial_vals<T, PER>(static_cast<T*>(a.p_o) + row * D + PER * lane, v);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -969,13 +1045,14 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
     }
   }
 
-  // this split's partials are written: publish them by counting this
-  // workgroup on the class's completion counter for its KV head
+  // this split's partials are written: count one arrival per request of the
+  // tile (its G rows for this KV head) for the requests' joins
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_fetch_add(a.done + static_cast<size_t>(ci) * a.n_kv + kv_head, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) {
+    if (lane < n_mem) arrive(a, mb0, kv_head);
+    if (lane + 64 < n_mem) arrive(a, mb1, kv_head);
+  }
 }
 
 // -------------------------------------------------------------- step kernel
@@ -991,18 +1068,31 @@ constexpr size_t step_smem_bytes() {
   return sizeof(PrefixSmem<T, D>) > sizeof(SuffixSmem<T, D>) ? sizeof(PrefixSmem<T, D>) : sizeof(SuffixSmem<T, D>);
 }
 
+// Join of (request b, KV head g): waits for the arrival of all partials,
+// then wave w joins the request's query heads g*G + w, g*G + w + 4, ...
+template <typename T, int D>
+__device__ __forceinline__ void join_block(const StepArgs& a, int j) {
+  const int b = j / a.n_kv, g = j - (j / a.n_kv) * a.n_kv;
+  const int n = partials_of(a, b);
+  if (n == 1) return;   // finished by its only suffix part
+  if (threadIdx.x == 0) wait_arrivals(a, b, g, n);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int col = wave; col < a.group; col += kWaves) join_row<T, D>(a, b, g * a.group + col, lane);
+}
+
 template <typename T, int D, int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
-  __shared__ int32_t join_flag;
   const int blk = blockIdx.x;
-  if (blk < a.prefix_blocks) {
-    prefix_block<T, D, RB>(a, blk, smem);
-  } else {
-    const int sb = blk - a.prefix_blocks;
-    if (sb < a.suffix_blocks) suffix_block<T, D>(a, sb, smem, join_flag);
+  const int work = a.prefix_blocks + a.suffix_blocks;
+  if (blk >= work) {
+    join_block<T, D>(a, blk - work);
+    return;
   }
+  if (blk < a.prefix_blocks) prefix_block<T, D, RB>(a, blk, smem);
+  else suffix_block<T, D>(a, blk - a.prefix_blocks, smem);
 }
 
 __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, const u32x4* v_new,
@@ -1025,15 +1115,16 @@ hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, 
   // With timing events, the kernel is launched through hipExtLaunchKernelGGL,
   // which stamps the events with the kernel's own start and end.
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
-  const int blocks = a.prefix_blocks + a.suffix_blocks;
-  if (backend == 2) {
+  const int blocks = a.prefix_blocks + a.suffix_blocks + a.join_blocks;
+  (void)backend;
+  if (a.rb == 2) {
     if constexpr (sizeof(T) == 2) {
-      hipExtLaunchKernelGGL(step_kernel<T, D, kDenseRB>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+      hipExtLaunchKernelGGL(step_kernel<T, D, 2>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    hipExtLaunchKernelGGL(step_kernel<T, D, kCascadeRB>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(step_kernel<T, D, 1>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
   }
   return hipGetLastError();
 }

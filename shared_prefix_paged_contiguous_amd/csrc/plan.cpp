@@ -8,7 +8,6 @@ namespace gkv {
 
 namespace {
 
-constexpr int32_t kTargetBlocks = 512;      // prefix workgroups to aim for
 constexpr int32_t kMinSplitTokens = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -120,7 +119,12 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   // ---- prefix splits: one split length for all classes so that the total
   // work (KV heads x M-tiles x tokens) spreads over about kTargetBlocks
   // workgroups, with at least kMinSplitTokens tokens per split.
-  const int32_t rb = backend == GKV_BACKEND_DENSE ? kDenseRB : kCascadeRB;
+  int32_t max_rows = 0;
+  for (int32_t c = 0; c < n_classes; ++c) max_rows = std::max(max_rows, class_size[c] * group);
+  const int32_t rb = shape.bf16 && (backend == GKV_BACKEND_DENSE || max_rows > kSmallTileRows) ? 2 : 1;
+  a.rb = rb;
+  plan.rb = rb;
+  const int32_t target = backend == GKV_BACKEND_DENSE ? kDenseTarget : kCascadeTarget;
   const int32_t tm = tile_members(group, rb);
   if (tm < 1) {
     err = "query group of " + std::to_string(group) + " heads exceeds one prefix tile";
@@ -130,7 +134,7 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   for (int32_t c = 0; c < n_classes; ++c)
     units += static_cast<int64_t>(n_kv) * ceil_div(class_size[c], tm) * a.classes[c].len;
   const int64_t split_tokens = std::max<int64_t>(
-      kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), kTargetBlocks), kPrefixTile));
+      kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), target), kPrefixTile));
   int32_t max_splits = 0;
   int32_t blocks = 0;
   for (int32_t c = 0; c < n_classes; ++c) {
@@ -145,13 +149,13 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     cd.n_groups = n_kv * cd.n_splits;
     cd.block_base = blocks;
     cd.n_blocks = kXcds * static_cast<int32_t>(ceil_div(cd.n_groups, kXcds)) * cd.m_tiles;
-    cd.done_target = 0;   // set by the caller from its running totals
+    cd.pad_ = 0;
     blocks += cd.n_blocks;
     max_splits = std::max(max_splits, cd.n_splits);
   }
-  a.prefix_blocks = blocks;
+  a.prefix_blocks = static_cast<int32_t>(round_up(blocks, kGroup));
   a.max_splits = max_splits;
-  plan.prefix_blocks = blocks;
+  plan.prefix_blocks = a.prefix_blocks;
   plan.prefix_rows = static_cast<int64_t>(batch) * max_splits * n_q;
 
   // ---- suffix parts, longest slot table first (so the longest workgroups
@@ -173,16 +177,19 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     if (np > 1) multi = 1;
     parts += np;
   }
-  if (parts * n_kv > 0x7fffffffLL) {
+  if ((parts + kGroup) * n_kv + static_cast<int64_t>(batch) * n_kv + blocks > 0x7fffffffLL) {
     err = "too many suffix parts";
     return -1;
   }
   a.part_start[batch] = static_cast<int32_t>(parts);
-  a.suffix_blocks = static_cast<int32_t>(parts * n_kv);
+  a.suffix_blocks = static_cast<int32_t>(round_up(parts * n_kv, kGroup));
   a.multi_part = multi;
   a.need_merge = multi || n_classes > 0;
+  a.join_blocks = a.need_merge ? batch * n_kv : 0;
   plan.n_parts = static_cast<int32_t>(parts);
+  plan.part_tokens = kSuffixPart;
   plan.suffix_blocks = a.suffix_blocks;
+  plan.join_blocks = a.join_blocks;
   plan.multi_part = a.need_merge;
   plan.suffix_rows = a.need_merge ? parts * n_q : 0;
   return 0;

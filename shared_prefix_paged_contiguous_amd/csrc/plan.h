@@ -1,6 +1,6 @@
 // Host planner of one decode step: class grouping, the per-step backend rule
-// and the work decomposition of the prefix, suffix and merge kernels, all
-// written into the kernel-argument block (StepArgs).  Pure C++.
+// and the work decomposition of the step kernel (prefix splits, suffix parts,
+// joins), all written into the kernel-argument block (StepArgs).  Pure C++.
 //
 // Class grouping: paperlayer.ai summary of the GraniKV paper, Appendix B.8
 // (each distinct prefix is batched against its own slab, "class-local"
@@ -19,6 +19,7 @@ namespace gkv {
 
 struct PlanShape {
   int32_t n_q, n_kv, head_dim;
+  bool bf16;
 };
 
 struct Plan {
@@ -26,11 +27,14 @@ struct Plan {
   int32_t m_eff = 0;
   int32_t n_classes = 0;
   int32_t prefix_blocks = 0;    // prefix workgroups (including idle XCD padding)
-  int32_t suffix_blocks = 0;    // suffix workgroups
+  int32_t suffix_blocks = 0;    // suffix workgroups (incl. padding)
+  int32_t join_blocks = 0;      // join workgroups
   int32_t n_parts = 0;          // suffix parts (>= one per request)
   int32_t multi_part = 0;       // some request's output is joined from several partials
   int64_t prefix_rows = 0;      // prefix partial rows (B * max_splits * n_q)
   int64_t suffix_rows = 0;      // suffix partial rows
+  int32_t part_tokens = 0;      // slot-table tokens per suffix part
+  int32_t rb = 1;               // row blocks per wave of the prefix tiles
 };
 
 // Rule alone: dense iff batch * group >= m_sat (unless forced).

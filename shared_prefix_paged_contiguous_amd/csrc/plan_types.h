@@ -16,8 +16,16 @@ namespace gkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPrefixTile = 64;
-constexpr int kCascadeRB = 1;     // cascade backend: 64-row tiles, many L splits
-constexpr int kDenseRB = 2;       // dense backend: 128-row tiles (batched GEMM)
+// Row blocks per wave of a prefix tile (RB): 2 (128-row tiles, each LDS read
+// of a block feeds two row blocks) when some class has more than 64 rows
+// per KV head and the dtype is bf16, else 1 (64-row tiles).
+constexpr int kSmallTileRows = 64;
+// Prefix workgroups a step aims for: the cascade backend (memory-bound
+// regime) leaves half of the chip's workgroup slots to the suffix gather,
+// which runs alongside; the dense backend (compute-bound regime) spreads
+// the prefix GEMM over all of them.
+constexpr int kCascadeTarget = 256;
+constexpr int kDenseTarget = 512;
 constexpr int kSuffixTile = 32;   // suffix kernel token tile (per wave)
 constexpr int kWaveTokens = 1024; // most slot-table tokens one suffix wave covers (ids staged in LDS)
 constexpr int kSuffixPart = kWaves * kWaveTokens;   // tokens per suffix workgroup
@@ -50,7 +58,7 @@ struct ClassDesc {
   int32_t n_groups;     // n_kv * n_splits
   int32_t block_base;   // first prefix block
   int32_t n_blocks;     // 8 * ceil(n_groups / 8) * m_tiles
-  uint32_t done_target; // value of the class's completion counters once this step's splits are in
+  int32_t pad_;
 };
 
 // Suffix work: one workgroup per (suffix part, KV head).  Requests are
@@ -60,18 +68,24 @@ struct ClassDesc {
 // and the 4 waves take consecutive quarters of it.  Block i -> part
 // i / n_kv, KV head i % n_kv.  A request with no HOT prefix and one part is
 // finished in the suffix workgroup's epilogue.  Otherwise every prefix split
-// and suffix part writes a partial per (request, query head).  A prefix
-// workgroup then bumps its class's completion counter for its KV head; the
-// suffix part of (request, KV head) that arrives last among the request's
-// parts waits until that counter reaches done_target and joins the partials
-// into the output (no separate merge pass).  Prefix workgroups precede all
-// suffix workgroups in the grid and wait on nothing, so the wait ends.
+// and suffix part writes a partial per (request, query head) and counts its
+// arrival on the (request, KV head) counter; a join workgroup per (request,
+// KV head), placed after all prefix and suffix work in the grid, waits for
+// the count and joins the partials into the output.
+//
+// Grid: prefix blocks, then suffix blocks, then batch * n_kv join blocks.
+// Prefix and suffix blocks never wait, and every join block follows all of
+// them in each XCD's (in-order) dispatch, so the joins' waits end.
+constexpr int kGroup = 4 * kXcds;   // padding unit of the prefix and suffix ranges
+
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
   int32_t n_classes;
-  int32_t prefix_blocks;       // sum of class n_blocks
-  int32_t suffix_blocks;       // n_parts * n_kv
+  int32_t rb;                  // row blocks per wave of the prefix tiles (1 or 2)
+  int32_t prefix_blocks;       // sum of class n_blocks, padded to a multiple of kGroup
+  int32_t suffix_blocks;       // n_parts * n_kv, padded to a multiple of kGroup
+  int32_t join_blocks;         // batch * n_kv when some output is joined, else 0
   int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
   int32_t multi_part;          // some request has more than one suffix part
   int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
@@ -86,12 +100,11 @@ struct StepArgs {
   int32_t cold_cap;
   int32_t pad2_;
   const int32_t* cold_indices; // dev
-  float* p_o;                  // prefix partials [rows][head_dim], normalised
+  void* p_o;                   // prefix partials [rows][head_dim], normalised, in the input dtype
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
-  float* s_o;                  // suffix-part partials, row = part * n_q + h
+  void* s_o;                   // suffix-part partials, row = part * n_q + h (input dtype)
   float* s_lse;
-  int32_t* counters;           // [kMaxBatch][n_kv] suffix-part arrivals (zero between calls)
-  uint32_t* done;              // [kMaxClasses][n_kv] prefix-workgroup completions (running totals)
+  int32_t* counters;           // [kMaxBatch][n_kv] partial arrivals (zero between calls)
   ClassDesc classes[kMaxClasses];
   int32_t indptr[kMaxBatch + 1];        // slot-table row pointers (host copy of cold_indptr)
   int32_t part_start[kMaxBatch + 1];    // by rank

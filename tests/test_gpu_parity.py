@@ -321,13 +321,16 @@ def test_full_size_sampled_requests(name):
 
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_long_suffixes_span_several_parts(force):
-    """Slot tables longer than one suffix workgroup's share (4096 tokens) are
-    split into parts joined inside the step kernel; mixed with single-part
-    requests and a prefix-only request."""
+    """Slot tables longer than one suffix part are split into parts joined
+    inside the step kernel; mixed with single-part requests and a prefix-only
+    request.  The part length follows the step's total work."""
     s = spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
              fixed_suffix=(5000, 10, 0, 9000))
     w = workloads.make(s)
     st, out, lse, _ = run(w, force=force)
     plan = st.ctx.last_plan()
-    assert plan["joins_partials"] == 1 and plan["n_suffix_parts"] == 2 + 1 + 1 + 3
+    pt = plan["suffix_part_tokens"]
+    assert pt % 32 == 0 and 64 <= pt <= 4096
+    assert plan["joins_partials"] == 1
+    assert plan["n_suffix_parts"] == sum(max(1, -(-n // pt)) for n in (5000, 10, 0, 9000))
     check(out, lse, *oracle_ref(w))
