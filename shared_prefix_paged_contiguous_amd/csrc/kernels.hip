@@ -491,46 +491,123 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
 }
 
 // ------------------------------------------------------- in-kernel join
-// Partials of request b for query head h: its HOT class's n_splits prefix
-// splits (rows (b * max_splits + s) * n_q + h of p_o / p_lse) and its suffix
-// parts (rows part * n_q + h of s_o / s_lse).  One wave joins them by
-// log-sum-exp and writes out[b][h] (input dtype) and lse[b][h] (natural log).
-template <typename T, int D>
-__device__ __forceinline__ void join_row(const StepArgs& a, int b, int h, int lane) {
-  constexpr int PER = D / 64;
+// Where the partials of request b come from: its HOT class's n_splits prefix
+// splits (rows (b * max_splits + s) * n_q + h of p_o / p_lse) and its
+// n_parts suffix parts from part c0 on (rows part * n_q + h of s_o / s_lse).
+struct JoinSrc {
+  int ns, c0, n_parts;
+};
+__device__ __forceinline__ JoinSrc join_src(const StepArgs& a, int b) {
   const int r = a.rank_of[b];
-  const int c0 = a.part_start[r];
-  const int nparts = a.part_start[r + 1] - c0;
   const int cls = a.req_class[b];
-  const int ns = cls >= 0 ? a.classes[cls].n_splits : 0;
-  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
-  float acc[PER];
-  const float l2 = join_parts<PER, 32>(
-      ns + nparts, lane,
-      [&](int p) {
-        return load_partial(p < ns ? a.p_lse + prow0 + static_cast<size_t>(p) * a.n_q
-                                   : a.s_lse + static_cast<size_t>(c0 + p - ns) * a.n_q + h);
-      },
-      [&](int p, float (&v)[PER]) {
-        const T* po = static_cast<const T*>(a.p_o);
-        const T* so = static_cast<const T*>(a.s_o);
-        load_partial_vals<T, PER>(p < ns ? po + (prow0 + static_cast<size_t>(p) * a.n_q) * D + PER * lane
-                                         : so + (static_cast<size_t>(c0 + p - ns) * a.n_q + h) * D + PER * lane,
-                                  v);
-      },
-      acc);
-  T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + PER * lane;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
-  if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + h] = l2 * 0.69314718055994531f;
+  JoinSrc s;
+  s.ns = cls >= 0 ? a.classes[cls].n_splits : 0;
+  s.c0 = a.part_start[r];
+  s.n_parts = a.part_start[r + 1] - s.c0;
+  return s;
 }
 
-// Number of partials request b's output is joined from, per KV head: its
-// class's prefix splits and its suffix parts.
-__device__ __forceinline__ int partials_of(const StepArgs& a, int b) {
-  const int r = a.rank_of[b];
-  const int cls = a.req_class[b];
-  return (cls >= 0 ? a.classes[cls].n_splits : 0) + a.part_start[r + 1] - a.part_start[r];
+// 16 bytes of a partial row with two agent-scope 64-bit loads
+__device__ __forceinline__ u32x4 load_partial_chunk(const void* src) {
+  const uint64_t* p = static_cast<const uint64_t*>(src);
+  const uint64_t lo = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32), static_cast<uint32_t>(hi),
+               static_cast<uint32_t>(hi >> 32)};
+}
+// the 16 / sizeof(T) values of a 16-byte chunk
+template <typename T>
+__device__ __forceinline__ void unpack_chunk(const u32x4& w, float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+      v[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x = w[k];   // a scalar copy: bit_cast of a vector-element lvalue reads element 0
+      v[k] = __builtin_bit_cast(float, x);
+    }
+  }
+}
+
+// One wave joins the partials of request b for query head h by log-sum-exp
+// and writes out[b][h] (input dtype) and lse[b][h] (natural log).  Lane l
+// reads 16-byte chunk l % CH of partial rows l / CH, l / CH + 64 / CH, ...,
+// so one wave-wide access covers 64 / CH rows and a batch of up to 32
+// partials is a handful of independent loads issued back to back (indices
+// past the last partial repeat it and weigh zero).  The lane groups then sum
+// their chunks with cross-lane adds.
+template <typename T, int D>
+__device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, int b, int h, int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;                                 // rows per wave-wide access
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));      // values per chunk
+  constexpr int NB = 32;                                       // partials per batch
+  constexpr int NL = NB / RPI;                                 // chunk loads per lane per batch
+  static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
+  const int ns = src.ns, c0 = src.c0, np = ns + src.n_parts;
+  const int ch = lane % CH, rg = lane / CH;
+  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
+  auto row_of = [&](int p) -> size_t {   // row of partial p in p_o / p_lse (p < ns) or s_o / s_lse
+    return p < ns ? prow0 + static_cast<size_t>(p) * a.n_q : static_cast<size_t>(c0 + p - ns) * a.n_q + h;
+  };
+  auto lse_of = [&](int p) { return load_partial((p < ns ? a.p_lse : a.s_lse) + row_of(p)); };
+  auto chunk_of = [&](int p) {
+    const T* base = static_cast<const T*>(p < ns ? a.p_o : a.s_o);
+    return load_partial_chunk(base + row_of(p) * D + EPC * ch);
+  };
+  auto wave_max = [](float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+
+  float mx = kNegInf;
+  if (np > NB) {   // more partials than one batch: the common reference point first
+    for (int base = 0; base < np; base += 64) mx = fmaxf(mx, base + lane < np ? lse_of(base + lane) : kNegInf);
+    mx = wave_max(mx);
+  }
+  float acc[EPC];
+#pragma unroll
+  for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+  float wsum = 0.f;
+  for (int base = 0; base < np; base += NB) {
+    const int cnt = min(NB, np - base);
+    const float lp = lane < cnt ? lse_of(base + lane) : kNegInf;
+    u32x4 raw[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) raw[i] = chunk_of(base + min(i * RPI + rg, cnt - 1));
+    if (np <= NB) mx = wave_max(lp);
+    const float wl = lane < cnt && lp != kNegInf ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
+    wsum += wl;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float w = __shfl(wl, i * RPI + rg);   // zero for rows past cnt
+      float v[EPC];
+      unpack_chunk<T>(raw[i], v);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] += w * v[j];
+    }
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] += __shfl_xor(acc[j], off);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  // no tokens in any part: an empty result, o = 0 and lse = -inf
+  const bool empty = !(wsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / wsum;
+  if (rg == 0) {
+    T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + EPC * ch;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) dst[k] = static_cast<T>(acc[k] * inv);
+  }
+  if (lane == 0)
+    a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
 }
 
 // Counts the arrival of one partial of (request b, KV head g).  Protocol:
@@ -1070,15 +1147,18 @@ constexpr size_t step_smem_bytes() {
 
 // Join of (request b, KV head g): waits for the arrival of all partials,
 // then wave w joins the request's query heads g*G + w, g*G + w + 4, ...
+// Where the partials lie is read before the wait, so after it only the
+// partials themselves are loaded.
 template <typename T, int D>
 __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
   const int b = j / a.n_kv, g = j - (j / a.n_kv) * a.n_kv;
-  const int n = partials_of(a, b);
+  const JoinSrc src = join_src(a, b);
+  const int n = src.ns + src.n_parts;
   if (n == 1) return;   // finished by its only suffix part
   if (threadIdx.x == 0) wait_arrivals(a, b, g, n);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int col = wave; col < a.group; col += kWaves) join_row<T, D>(a, b, g * a.group + col, lane);
+  for (int col = wave; col < a.group; col += kWaves) join_row<T, D>(a, src, b, g * a.group + col, lane);
 }
 
 template <typename T, int D, int RB>
