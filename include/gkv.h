@@ -63,7 +63,7 @@ enum {
 };
 
 typedef struct {
-  int32_t n_q_heads;             /* query heads; a multiple of n_kv_heads */
+  int32_t n_q_heads;             /* query heads (<= 256); a multiple of n_kv_heads */
   int32_t n_kv_heads;            /* KV heads; n_q/n_kv (the group G) in 1..16 */
   int32_t head_dim;              /* 64 or 128 */
   int32_t dtype;                 /* GKV_F32 or GKV_BF16: q, K, V and out */

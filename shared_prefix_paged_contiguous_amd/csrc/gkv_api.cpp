@@ -23,6 +23,7 @@ namespace {
 // never slower than the cascade one, from the dispatcher fit over the
 // Qwen-2.5-14B and Llama-3.1-8B head shapes at L_p = 16K.
 constexpr int32_t kDefaultMSat = 1024;
+constexpr int32_t kMaxQHeads = 256;
 
 struct Layer {
   void* k_hot = nullptr;
@@ -105,6 +106,8 @@ int gkv_create(const gkv_config* cfg, gkv_ctx** out) {
   if (!cfg) return GKV_ERR_INVALID;
   const gkv_config& c = *cfg;
   if (c.n_q_heads <= 0 || c.n_kv_heads <= 0 || c.n_q_heads % c.n_kv_heads != 0) return GKV_ERR_INVALID;
+  // partial-row indices (request x split x query head) stay 32-bit
+  if (c.n_q_heads > kMaxQHeads) return GKV_ERR_INVALID;
   const int32_t group = c.n_q_heads / c.n_kv_heads;
   if (group > 16) return GKV_ERR_INVALID;
   if (c.head_dim != 64 && c.head_dim != 128) return GKV_ERR_INVALID;

@@ -73,6 +73,18 @@ __device__ __forceinline__ int tau(int g, int e) {
   return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
 }
 
+// Entry i of a 4-byte-aligned int16 / int8 table in the kernel arguments,
+// read through its aligned 32-bit word: there are no 8- or 16-bit scalar
+// loads, so a wave-uniform i then stays a scalar-cache read instead of a
+// vector memory round trip.
+template <typename I>
+__device__ __forceinline__ int table_at(const I* t, int i) {
+  constexpr int kBits = 8 * static_cast<int>(sizeof(I));
+  constexpr int kPer = 4 / static_cast<int>(sizeof(I));
+  const uint32_t w = reinterpret_cast<const uint32_t*>(t)[i / kPer];
+  return static_cast<int32_t>(w << (32 - kBits - (i % kPer) * kBits)) >> (32 - kBits);
+}
+
 __device__ __forceinline__ float wave_max_groups(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   return fmaxf(x, __shfl_xor(x, 32));
@@ -494,16 +506,20 @@ __device__ __forceinline__ float join_parts(int np, int lane, LseF lse_of, RowF 
 // Where the partials of request b come from: its HOT class's n_splits prefix
 // splits (rows (b * max_splits + s) * n_q + h of p_o / p_lse) and its
 // n_parts suffix parts from part c0 on (rows part * n_q + h of s_o / s_lse).
+// suffix parts of a ranked request: at least one
+__device__ __forceinline__ int parts_of(const RankDesc& rd) {
+  return max(1, static_cast<int>((static_cast<int64_t>(rd.tok1) - rd.tok0 + kSuffixPart - 1) / kSuffixPart));
+}
 struct JoinSrc {
   int ns, c0, n_parts;
 };
 __device__ __forceinline__ JoinSrc join_src(const StepArgs& a, int b) {
-  const int r = a.rank_of[b];
-  const int cls = a.req_class[b];
+  const RankDesc rd = a.ranks[table_at(a.rank_of, b)];
+  const int cls = table_at(a.req_class, b);
   JoinSrc s;
   s.ns = cls >= 0 ? a.classes[cls].n_splits : 0;
-  s.c0 = a.part_start[r];
-  s.n_parts = a.part_start[r + 1] - s.c0;
+  s.c0 = rd.part0;
+  s.n_parts = parts_of(rd);
   return s;
 }
 
@@ -665,16 +681,23 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int part = blk / a.n_kv;
   const int gk = blk - part * a.n_kv;
-  if (part >= a.part_start[a.batch]) return;   // grid padding
-  int lo = 0, hi = a.batch - 1;     // rank: last r with part_start[r] <= part
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.part_start[mid] <= part) lo = mid; else hi = mid - 1;
+  if (part >= a.n_parts) return;   // grid padding
+  // rank: the last r with ranks[r].part0 <= part, which is the part itself
+  // when every request has one part
+  int lo = part;
+  if (a.multi_part) {
+    lo = 0;
+    int hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.ranks[mid].part0 <= part) lo = mid; else hi = mid - 1;
+    }
   }
-  const int b = a.order[lo];
-  const int j = part - a.part_start[lo];
-  const bool single = a.part_start[lo + 1] - a.part_start[lo] == 1;
-  const int tb0 = a.indptr[b], tb1 = a.indptr[b + 1];
+  const RankDesc rd = a.ranks[lo];
+  const int b = rd.req;
+  const int j = part - rd.part0;
+  const bool single = parts_of(rd) == 1;
+  const int tb0 = rd.tok0, tb1 = rd.tok1;
   const int p0 = min(tb1, tb0 + j * kSuffixPart), p1 = min(tb1, p0 + kSuffixPart);
   const int piece = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
   const int w0 = min(p1, p0 + wave * piece), w1 = min(p1, w0 + piece);
@@ -691,11 +714,6 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
 #pragma unroll
   for (int k = 0; k < D / 4; ++k) o[k] = 0.f;
   if (len > 0) {
-    ColState<T, D> st;
-    st.init();
-    if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
-    else TR::zero_row(st.q);
-
     const size_t stride = static_cast<size_t>(a.n_kv) * D;
     const T* kc = static_cast<const T*>(a.k_cold) + gk * D;
     const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
@@ -703,12 +721,25 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     const int cap1 = a.cold_cap - 1;
 
     // the piece's slot ids, clamped into the pool, staged in this wave's
-    // LDS row once: no tile waits on a slot-id load
+    // LDS row once: no tile waits on a slot-id load.  The loads of 256 ids
+    // are issued before the first is used (one round trip per 256 ids).
     int32_t* ids = lds_ids[wave];
-    for (int k = lane; k < len; k += 64) ids[k] = min(max(a.cold_indices[w0 + k], 0), cap1);
+    for (int base = 0; base < len; base += 256) {
+      int32_t raw[4];
+#pragma unroll
+      for (int ck = 0; ck < 4; ++ck) raw[ck] = a.cold_indices[w0 + min(base + 64 * ck + lane, len - 1)];
+#pragma unroll
+      for (int ck = 0; ck < 4; ++ck)
+        if (base + 64 * ck + lane < len) ids[base + 64 * ck + lane] = min(max(raw[ck], 0), cap1);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the query row after the slot ids: the ids' wait does not cover it
+    ColState<T, D> st;
+    st.init();
+    if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
+    else TR::zero_row(st.q);
 
     auto load_kv = [&](int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
       const int base = kSuffixTile * i, last = len - 1;
@@ -751,7 +782,7 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   __syncthreads();
 
   // epilogue: wave w joins columns w, w+4, ... over the four pieces
-  const bool final_here = single && a.req_class[b] < 0;
+  const bool final_here = single && table_at(a.req_class, b) < 0;
   for (int col = wave; col < G; col += kWaves) {
     const int hc = gk * G + col;
     float acc[PER];
@@ -958,13 +989,20 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
     for (int cp = 0; cp < kCopies; ++cp)
       load_lds_1k(voff, src0[cp] + static_cast<size_t>(i) * kImg, dst0[cp] + slot * (2 * kImg));
   };
+  // the tile's request ids, one per lane (tile_members <= 128), loaded once
+  // without a branch: query rows and partial rows find theirs by lane reads
+  static_assert(kWaves * 16 * 2 <= 128, "tile members exceed two lanes' worth");
+  const int mb0 = a.members[cl.member_off + mem0 + min(lane, n_mem - 1)];
+  const int mb1 = a.members[cl.member_off + mem0 + min(lane + 64, n_mem - 1)];
   ColState<T, D> st[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     st[rb].init();
     const int r = wrow0 + 16 * rb + n;
+    const int k = r / G;
+    const int b0 = __shfl(mb0, k & 63), b1 = __shfl(mb1, k & 63);
     if (r < rows) {
-      const int b = a.members[cl.member_off + mem0 + r / G];
+      const int b = k < 64 ? b0 : b1;
       const int h = kv_head * G + r % G;
       TR::load_row(st[rb].q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
     } else {
@@ -1074,15 +1112,6 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   constexpr int kStride = D + 4;   // padded row stride of the staging tile (floats)
   static_assert(kWaves * 16 * kStride * 4 <= kStages * 2 * kImg, "staging tile exceeds the ring");
   float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 16 * kStride;
-  // the tile's request ids, one per lane (tile_members <= 128): rows then
-  // find theirs with a lane read instead of a dependent load per row
-  const int mb0 = lane < n_mem ? a.members[cl.member_off + mem0 + lane] : 0;
-  const int mb1 = lane + 64 < n_mem ? a.members[cl.member_off + mem0 + 64 + lane] : 0;
-  auto member_of_row = [&](int ri) {   // ri wave-uniform
-    const int k = ri / G;
-    return k < 64 ? __builtin_amdgcn_readlane(mb0, k) : __builtin_amdgcn_readlane(mb1, k - 64);
-  };
-  static_assert(kWaves * 16 * 2 <= 128, "tile members exceed two lanes' worth");
   if (wave_active) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -1092,29 +1121,32 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       for (int k = 0; k < D / 16; ++k)
         *reinterpret_cast<f32x4*>(stage + n * kStride + (D / 4) * g + 4 * k) =
             f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-      // lse of row n: move it to lane n, then lanes < 16 store
+      // partial row index of tile row wrow0 + 16 rb + l, computed once by
+      // lane l (< 16, one division by G for all rows); the lse of row n
+      // moves to lane n and lanes < 16 store it
       const float lse_n = __shfl(lse2, n);
-      const int r = wrow0 + 16 * rb + lane;
+      const int r = wrow0 + 16 * rb + n;
       const int kr = r / G;
-      const int bl0 = __shfl(mb0, kr % 64), bl1 = __shfl(mb1, kr % 64);
+      const int bl0 = __shfl(mb0, kr & 63), bl1 = __shfl(mb1, kr & 63);
       const int bl = kr < 64 ? bl0 : bl1;
-      if (lane < 16 && r < rows) {
-        const size_t row = (static_cast<size_t>(bl) * a.max_splits + split) * a.n_q + kv_head * G + r % G;
-        store_partial(a.p_lse + row, lse_n);
-      }
+      const int prow = (bl * a.max_splits + split) * a.n_q + kv_head * G + (r - kr * G);
+      if (lane < 16 && r < rows) store_partial(a.p_lse + prow, lse_n);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // all 16 rows leave LDS before the first store (one LDS wait, not 16)
       constexpr int PER = D / 64;
-      for (int i = 0; i < 16; ++i) {
-        const int ri = wrow0 + 16 * rb + i;
-        if (ri >= rows) break;
-        const int b = member_of_row(ri);
-        const size_t row = (static_cast<size_t>(b) * a.max_splits + split) * a.n_q + kv_head * G + ri % G;
-        float v[PER];
+      float v[16][PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) v[j] = stage[i * kStride + PER * lane + j];
-        store_partial_vals<T, PER>(static_cast<T*>(a.p_o) + row * D + PER * lane, v);
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[i][j] = stage[i * kStride + PER * lane + j];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (wrow0 + 16 * rb + i < rows) {
+          const size_t row = static_cast<uint32_t>(__builtin_amdgcn_readlane(prow, i));
+          store_partial_vals<T, PER>(static_cast<T*>(a.p_o) + row * D + PER * lane, v[i]);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1165,6 +1197,7 @@ template <typename T, int D, int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
+  if (a.tail != kArgsTail) return;   // the work description did not arrive whole
   const int blk = blockIdx.x;
   const int work = a.prefix_blocks + a.suffix_blocks;
   if (blk >= work) {

@@ -160,7 +160,6 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
 
   // ---- suffix parts, longest slot table first (so the longest workgroups
   // start first and the kernel's tail is short)
-  for (int32_t b = 0; b <= batch; ++b) a.indptr[b] = indptr[b];
   int32_t order[kMaxBatch];
   for (int32_t b = 0; b < batch; ++b) order[b] = b;
   std::stable_sort(order, order + batch, [&](int32_t x, int32_t y) {
@@ -170,9 +169,8 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   int32_t multi = 0;
   for (int32_t r = 0; r < batch; ++r) {
     const int32_t b = order[r];
-    a.order[r] = static_cast<int16_t>(b);
     a.rank_of[b] = static_cast<int16_t>(r);
-    a.part_start[r] = static_cast<int32_t>(parts);
+    a.ranks[r] = RankDesc{indptr[b], indptr[b + 1], static_cast<int32_t>(parts), b};
     const int64_t np = std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
     if (np > 1) multi = 1;
     parts += np;
@@ -181,7 +179,8 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     err = "too many suffix parts";
     return -1;
   }
-  a.part_start[batch] = static_cast<int32_t>(parts);
+  a.n_parts = static_cast<int32_t>(parts);
+  a.tail = kArgsTail;
   a.suffix_blocks = static_cast<int32_t>(round_up(parts * n_kv, kGroup));
   a.multi_part = multi;
   a.need_merge = multi || n_classes > 0;

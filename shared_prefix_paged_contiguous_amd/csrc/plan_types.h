@@ -1,6 +1,6 @@
 // Work description of one decode step, shared by the host planner and the
 // device kernels.  The whole description travels in the kernel arguments
-// (about 15 KB), so a step needs no host-to-device copy before its kernels.
+// (about 21 KB), so a step needs no host-to-device copy before its kernels.
 #pragma once
 
 #include <cstdint>
@@ -62,9 +62,9 @@ struct ClassDesc {
 };
 
 // Suffix work: one workgroup per (suffix part, KV head).  Requests are
-// ranked longest slot table first; rank r owns parts [part_start[r],
-// part_start[r+1]) (at least one, so every request gets a merge epilogue);
-// part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
+// ranked longest slot table first; rank r owns parts [ranks[r].part0,
+// ranks[r].part0 + n) with n = max(1, ceil(table length / kSuffixPart))
+// (at least one, so every request gets a merge epilogue); part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
 // and the 4 waves take consecutive quarters of it.  Block i -> part
 // i / n_kv, KV head i % n_kv.  A request with no HOT prefix and one part is
 // finished in the suffix workgroup's epilogue.  Otherwise every prefix split
@@ -78,6 +78,13 @@ struct ClassDesc {
 // them in each XCD's (in-order) dispatch, so the joins' waits end.
 constexpr int kGroup = 4 * kXcds;   // padding unit of the prefix and suffix ranges
 
+// A ranked request's suffix work in one 16-byte record (one scalar load).
+struct RankDesc {
+  int32_t tok0, tok1;   // its slot-table range [tok0, tok1) in cold_indices
+  int32_t part0;        // its first suffix part
+  int32_t req;          // the request (batch index)
+};
+
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
@@ -88,6 +95,7 @@ struct StepArgs {
   int32_t join_blocks;         // batch * n_kv when some output is joined, else 0
   int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
   int32_t multi_part;          // some request has more than one suffix part
+  int32_t n_parts;             // suffix parts of the step
   int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
   const void* q;
   void* out;
@@ -106,12 +114,15 @@ struct StepArgs {
   float* s_lse;
   int32_t* counters;           // [kMaxBatch][n_kv] partial arrivals (zero between calls)
   ClassDesc classes[kMaxClasses];
-  int32_t indptr[kMaxBatch + 1];        // slot-table row pointers (host copy of cold_indptr)
-  int32_t part_start[kMaxBatch + 1];    // by rank
-  int16_t order[kMaxBatch];             // request of rank r
-  int16_t rank_of[kMaxBatch];           // rank of request b
-  int16_t members[kMaxBatch];           // requests grouped by class
-  int8_t req_class[kMaxBatch];          // class of request b, -1 = none
+  alignas(16) RankDesc ranks[kMaxBatch];   // by rank
+  // small-int tables, 4-byte aligned so entries can be read with 32-bit loads
+  alignas(4) int16_t rank_of[kMaxBatch];   // rank of request b
+  alignas(4) int16_t members[kMaxBatch];   // requests grouped by class
+  alignas(4) int8_t req_class[kMaxBatch];  // class of request b, -1 = none
+  // last word: the kernels do nothing unless it holds kArgsTail, so a work
+  // description that did not arrive whole is never acted on
+  int32_t tail;
 };
+constexpr int32_t kArgsTail = 0x47'4b'56'31;
 
 }  // namespace gkv

@@ -54,7 +54,7 @@ def _ctx(**kw):
 def test_create_rejects_bad_configs():
     _lib_or_skip()
     for kw in [dict(n_q_heads=10, n_kv_heads=4), dict(head_dim=96), dict(n_q_heads=34, n_kv_heads=2),
-               dict(hot_capacity_tokens=-1), dict(cold_capacity_tokens=2 ** 31),
+               dict(n_q_heads=264, n_kv_heads=33), dict(hot_capacity_tokens=-1), dict(cold_capacity_tokens=2 ** 31),
                dict(dtype="f32", force_backend=binding.BACKEND_DENSE)]:
         with pytest.raises(binding.GkvError):
             _ctx(**kw)
