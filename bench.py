@@ -277,45 +277,61 @@ def run_bench(args):
 
 
 def fit_msat(args):
-    """Time both prefix kernels (prefix-only steps) over a batch sweep and
-    report the smallest M_eff from which dense is never slower."""
+    """Re-fit the dispatcher threshold M_sat on this GPU.
+
+    For each workload and batch size, time the step kernel under both prefix
+    backends, once on full decode steps (the workload's suffix mix) and once
+    on prefix-only steps (a one-token suffix: the prefix kernels alone).
+    The fitted M_sat is the threshold t of the rule "dense iff M_eff >= t"
+    (t among the swept M_eff values, or past the largest) with the least
+    total relative regret sum(time(rule) / time(best) - 1) over the full-step
+    points of all workloads; prefix-only points are reported alongside."""
     import torch
 
     from shared_prefix_paged_contiguous_amd import binding, workloads
     from shared_prefix_paged_contiguous_amd.harness import DecodeState
 
+    def time_step(w, force, n_layers=2, warm=5, steps=20):
+        st = DecodeState(w, n_layers=n_layers, force_backend=force)
+        out, lse = st.new_outputs()
+        for i in range(warm):
+            st.run(out, lse, layer=i % n_layers)
+        st.ctx.kernel_timing(steps)
+        for i in range(steps):
+            st.run(out, lse, layer=i % n_layers)
+        us = float(st.ctx.kernel_timing_read(steps).mean()) * 1e3
+        del st
+        torch.cuda.empty_cache()
+        return us
+
     rows = []
     for name in args.fit_workloads.split(","):
         g = workloads.SPECS[name].n_q // workloads.SPECS[name].n_kv
         for bsz in [int(x) for x in args.fit_batches.split(",")]:
-            w = workloads.make(name, batch=bsz, suffix_range=(1, 1))
-            st = DecodeState(w, n_layers=2)
-            out, lse = st.new_outputs()
             res = {"workload": name, "batch": bsz, "m_eff": bsz * g}
-            for label, force in (("cascade", binding.BACKEND_CASCADE), ("dense", binding.BACKEND_DENSE)):
-                st.ctx.set_dispatch(force)
-                for i in range(5):
-                    st.run(out, lse, layer=i % 2)
-                st.ctx.kernel_timing(20)
-                for i in range(20):
-                    st.run(out, lse, layer=i % 2)
-                per = st.ctx.kernel_timing_read(20)
-                st.ctx.kernel_timing(0)
-                res[label + "_prefix_us"] = round(float(per.mean()) * 1e3, 2)   # whole call
+            for kind, kw in (("full", {}), ("prefix_only", {"suffix_range": (1, 1)})):
+                w = workloads.make(name, batch=bsz, **kw)
+                for label, force in (("cascade", binding.BACKEND_CASCADE), ("dense", binding.BACKEND_DENSE)):
+                    res[f"{kind}_{label}_us"] = round(time_step(w, force), 2)
                 flops = 4 * bsz * g * w.prefix_lens[0] * w.spec.head_dim * w.spec.n_kv
-                res[label + "_mfma_frac"] = round(float(flops / (per.mean() * 1e-3) / 1e12 / BF16_PEAK_TFLOPS), 4)
+                res[f"{kind}_dense_prefix_tflops"] = round(flops / (res[f"{kind}_dense_us"] * 1e-6) / 1e12, 1)
             rows.append(res)
             print(json.dumps(res), flush=True)
-            del st
-            torch.cuda.empty_cache()
-    for name in args.fit_workloads.split(","):
-        pts = sorted((r for r in rows if r["workload"] == name), key=lambda r: r["m_eff"])
-        m_sat = None
-        for i, r in enumerate(pts):
-            if all(p["dense_prefix_us"] <= p["cascade_prefix_us"] for p in pts[i:]):
-                m_sat = r["m_eff"]
-                break
-        print(json.dumps({"workload": name, "fitted_m_sat": m_sat}), flush=True)
+
+    def regret(t, pts, kind):
+        tot = 0.0
+        for r in pts:
+            c, d = r[f"{kind}_cascade_us"], r[f"{kind}_dense_us"]
+            tot += (d if r["m_eff"] >= t else c) / min(c, d) - 1.0
+        return tot
+
+    cands = sorted({r["m_eff"] for r in rows}) + [math.inf]
+    for kind in ("full", "prefix_only"):
+        best = min(cands, key=lambda t: (regret(t, rows, kind), t))
+        print(json.dumps({"fit": kind, "fitted_m_sat": None if best == math.inf else best,
+                          "regret": round(regret(best, rows, kind), 4),
+                          "per_workload": {n: round(regret(best, [r for r in rows if r["workload"] == n], kind), 4)
+                                           for n in args.fit_workloads.split(",")}}), flush=True)
 
 
 def main():
@@ -334,7 +350,7 @@ def main():
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--fit-msat", action="store_true")
     ap.add_argument("--fit-workloads", default="qwen14b_tp2_lp16k_b128,llama8b_lp16k_b64")
-    ap.add_argument("--fit-batches", default="8,16,32,64,128,192,256,384,512")
+    ap.add_argument("--fit-batches", default="8,16,32,64,128,256,384,512,768")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "

@@ -22,7 +22,13 @@ namespace {
 // M_sat on MI355X: the smallest M_eff from which the dense prefix kernel is
 // never slower than the cascade one, from the dispatcher fit over the
 // Qwen-2.5-14B and Llama-3.1-8B head shapes at L_p = 16K.
-constexpr int32_t kDefaultMSat = 1024;
+// Dispatcher threshold on M_eff = batch * (query heads per KV head).  Fit on
+// MI355X over full decode steps (Llama-3.1-8B and Qwen-2.5-14B attention
+// shapes, L_p = 16K, suffixes of 128..1024 tokens, M_eff 32..3840): the
+// cascade backend was at least as fast at every point up to 3840, where
+// the two tie, so dense is chosen only from 4096 on.  (The page's A100
+// figure is 1024.)
+constexpr int32_t kDefaultMSat = 4096;
 constexpr int32_t kMaxQHeads = 256;
 
 struct Layer {

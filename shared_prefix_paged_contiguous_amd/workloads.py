@@ -173,6 +173,11 @@ def make(name_or_spec, *, seed: Optional[int] = None, dtype: Optional[str] = Non
     else:
         suffix_lens = rng.integers(spec.suffix_lo, spec.suffix_hi + 1, size=n_b).astype(np.int64)
 
+    # a larger batch than the spec's (an M_eff sweep point) may need a larger
+    # COLD pool; specs that fit draw exactly as before
+    need = int(suffix_lens.sum()) + n_b
+    if need > spec.cold_capacity:
+        spec = dataclasses.replace(spec, cold_capacity=-(-need * 5 // 4 // 4096) * 4096)
     cold_perm = rng.permutation(spec.cold_capacity).astype(np.int32)
 
     q = _values(rng, (n_b, n_q, d), spec.dtype)
