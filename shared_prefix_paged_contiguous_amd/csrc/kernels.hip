@@ -373,6 +373,76 @@ __device__ __forceinline__ void tile_rows(ColState<T, D> (&st)[RB], const typena
   for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
 }
 
+// The same per-block arithmetic as tile_rows, in pieces for a software
+// pipeline that overlaps the QK^T products of the next block (matrix cores)
+// with the softmax of the current one (VALU).
+// S^T tiles of one block for the RB row blocks.
+template <typename T, int D, int RB>
+__device__ __forceinline__ void qk_rows(const ColState<T, D> (&st)[RB], const typename Traits<T, D>::KOp (&k0)[Traits<T, D>::KS],
+                                        const typename Traits<T, D>::KOp (&k1)[Traits<T, D>::KS], f32x4 (&s0)[RB],
+                                        f32x4 (&s1)[RB]) {
+  using TR = Traits<T, D>;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    s0[rb] = TR::qk(k0, st[rb].q);
+    s1[rb] = TR::qk(k1, st[rb].q);
+  }
+}
+// Masks tokens >= valid and moves the reference points (lazy rescaling, one
+// wave vote for all row blocks; rare).
+template <typename T, int D, int RB>
+__device__ __forceinline__ void softmax_ref(ColState<T, D> (&st)[RB], f32x4 (&s0)[RB], f32x4 (&s1)[RB], int valid, int g,
+                                            float c) {
+  using TR = Traits<T, D>;
+  if (valid < 32) {
+    int v = __builtin_amdgcn_readfirstlane(valid);
+    asm volatile("" : "+s"(v));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * g + i >= v) s0[rb][i] = kNegInf;
+        if (16 + 4 * g + i >= v) s1[rb][i] = kNegInf;
+      }
+  }
+  float lmx[RB];
+  bool jump = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    lmx[rb] = fmaxf(fmaxf(fmaxf(s0[rb][0], s0[rb][1]), fmaxf(s0[rb][2], s0[rb][3])),
+                    fmaxf(fmaxf(s1[rb][0], s1[rb][1]), fmaxf(s1[rb][2], s1[rb][3]))) * c;
+    jump = jump || lmx[rb] > st[rb].m + kLazy;
+  }
+  if (__any(jump)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ColState<T, D>& cs = st[rb];
+      const float m_new = fmaxf(cs.m, wave_max_groups(lmx[rb]));
+      const float alpha = __builtin_amdgcn_exp2f(cs.m - m_new);
+      cs.l *= alpha;
+#pragma unroll
+      for (int j = 0; j < TR::EPB; ++j) cs.acc[j] *= alpha;
+      cs.m = m_new;
+    }
+  }
+}
+// Probabilities of one block against the current reference points, and the
+// lanes' shares of the row sums.
+template <typename T, int D, int RB>
+__device__ __forceinline__ void softmax_p(ColState<T, D> (&st)[RB], const f32x4 (&s0)[RB], const f32x4 (&s1)[RB], float c,
+                                          f32x4 (&p0)[RB], f32x4 (&p1)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    ColState<T, D>& cs = st[rb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[rb][i], c, -cs.m));
+      p1[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[rb][i], c, -cs.m));
+    }
+    cs.l += (p0[rb][0] + p0[rb][1]) + (p0[rb][2] + p0[rb][3]) + (p1[rb][0] + p1[rb][1]) + (p1[rb][2] + p1[rb][3]);
+  }
+}
+
 // Partials cross workgroups (and XCDs, whose L2 caches are not coherent
 // with one another) inside one launch, so they are written and read with
 // agent-scope relaxed atomic accesses: these bypass the non-coherent cache
@@ -1021,20 +1091,14 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
 #pragma unroll
     for (int s2 = 0; s2 < TR::KS; ++s2) asm volatile("" : "+v"(st[rb].q[s2]));
 
-  // Pipeline: at the top of iteration i the K operands of block i (and its
-  // V operands where registers allow, kPipeV) are in registers or on their
-  // way from LDS, and copies of blocks up to i + kStages - 2 are issued.
-  // Iteration i waits for block i + 1, passes the barrier (after which block
-  // i - 1's slot is free: its operands were read by iteration i - 1), issues
-  // the copy of block i + kStages - 1 into that slot, starts reading block
-  // i + 1's operands and computes block i.  Without kPipeV the V operands
-  // are read at the start of the block's compute and land during QK^T and
-  // the softmax.  fp32 rows of 128 (kPipeK false) read everything in place.
+  // Where registers allow (kPipeK: K operands, the block's score tiles for
+  // two blocks and the V operands beside the state), the block loop is
+  // software-pipelined (below); fp32 rows of 128 read and compute each
+  // block in place.
   constexpr int kKRegs = 2 * TR::KS * static_cast<int>(sizeof(KOp)) / 4;
   constexpr int kVRegs = static_cast<int>(sizeof(typename TR::VOp)) / 4;
   constexpr int kStateRegs = RB * static_cast<int>(sizeof(ColState<T, D>)) / 4;
-  constexpr bool kPipeV = kStateRegs + 2 * (kKRegs + kVRegs) <= 180;
-  constexpr bool kPipeK = kStateRegs + 2 * kKRegs + kVRegs <= 180;
+  constexpr bool kPipeK = kStateRegs + kKRegs + kVRegs + 8 * RB <= 200;
   struct KOps { KOp k0[TR::KS], k1[TR::KS]; };
   struct Ops {
     KOps k;
@@ -1066,30 +1130,67 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   };
 
   if constexpr (kPipeK) {
-    auto step = [&](Ops& cur, Ops& nxt, int i) {
-      if (i + 1 < nb) {
-        wait_block(i + 1, min(nb - 1, i + kStages - 2));
-        if (i + kStages - 1 < nb) copy(i + kStages - 1, (i + kStages - 1) % kStages);
-        if (wave_active) {
-          if constexpr (!kPipeV) read_v(cur.vo, i);
-          read_k(nxt.k, i + 1);
-          if constexpr (kPipeV) read_v(nxt.vo, i + 1);
-        }
-      } else if (wave_active) {
-        if constexpr (!kPipeV) read_v(cur.vo, i);
-      }
-      if (wave_active) compute(cur.k, cur.vo, i);
-    };
-    Ops oa, ob;
+    // Software pipeline over blocks.  S(i) = QK^T of block i is computed in
+    // iteration i - 1, and its reference points are moved right after (rare
+    // branch).  Iteration i waits for block i + 1 and passes the barrier
+    // (block i - 1's slot is then free: its K was read in iteration i - 2,
+    // its V in i - 1), issues the copy of block i + kStages - 1, reads K(i+1)
+    // and V(i), then runs one branch-free region: the QK^T of block i + 1 on
+    // the matrix cores interleaved with the softmax of S(i) on the VALU, then
+    // PV(i); last, the reference points for S(i + 1).  Only the last block
+    // can be partial; it is masked when its scores are formed and done after
+    // the loop.
+    auto valid_of = [&](int j) { return min(kHotBlock, t1 - t0 - kHotBlock * j); };
+    f32x4 s0[RB], s1[RB];
     wait_block(0, min(nb - 1, kStages - 2));
     if (wave_active) {
-      read_k(oa.k, 0);
-      if constexpr (kPipeV) read_v(oa.vo, 0);
+      KOps k;
+      read_k(k, 0);
+      qk_rows<T, D, RB>(st, k.k0, k.k1, s0, s1);
+      softmax_ref<T, D, RB>(st, s0, s1, valid_of(0), g, c);
     }
-    for (int i = 0; i < nb; i += 2) {
-      step(oa, ob, i);
-      if (i + 1 >= nb) break;
-      step(ob, oa, i + 1);
+    for (int i = 0; i + 1 < nb; ++i) {
+      wait_block(i + 1, min(nb - 1, i + kStages - 2));
+      if (i + kStages - 1 < nb) copy(i + kStages - 1, (i + kStages - 1) % kStages);
+      if (wave_active) {
+        typename TR::VOp vo;
+        KOps k;
+        read_k(k, i + 1);
+        read_v(vo, i);
+        f32x4 n0[RB], n1[RB], p0[RB], p1[RB];
+        qk_rows<T, D, RB>(st, k.k0, k.k1, n0, n1);
+        softmax_p<T, D, RB>(st, s0, s1, c, p0, p1);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
+        // one MFMA of QK^T(i + 1), then VALU work of the softmax, repeated;
+        // the PV products follow
+#pragma unroll
+        for (int x = 0; x < 2 * RB * TR::KS; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        softmax_ref<T, D, RB>(st, n0, n1, valid_of(i + 1), g, c);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          s0[rb] = n0[rb];
+          s1[rb] = n1[rb];
+        }
+      }
+    }
+    if (wave_active) {
+      const int i = nb - 1;
+      typename TR::VOp vo;
+      read_v(vo, i);
+      const int valid = valid_of(i);
+      if (valid < kHotBlock) {
+        int v = __builtin_amdgcn_readfirstlane(valid);
+        asm volatile("" : "+s"(v));
+        TR::mask_v(vo, v, g);
+      }
+      f32x4 p0[RB], p1[RB];
+      softmax_p<T, D, RB>(st, s0, s1, c, p0, p1);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
     }
   } else {
     for (int i = 0; i < nb; ++i) {
