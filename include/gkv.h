@@ -198,6 +198,30 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
                     const int32_t* cold_indptr_d, const int32_t* cold_indices_d,
                     void* out, float* lse, void* stream, int32_t* backend_out);
 
+/* One whole decode step in one launch: the batch's new tokens are appended to
+ * COLD and every request attends its context including its new token
+ * (paperlayer.ai §1 "Design": decoded tokens go to COLD; §2 "Prefix-suffix
+ * attention").  Same result as gkv_cold_append(ctx, layer, k_new, v_new,
+ * new_slots_d, B, stream) followed by gkv_attn_decode(...) with the same
+ * other arguments, provided that for every request b new_slots_d[b] is the
+ * last entry of b's slot table (its decode token); otherwise the result is
+ * unspecified.
+ *   k_new, v_new  dev [B][n_kv][head_dim], cfg.dtype, 16-byte aligned: the
+ *                 new token of request b
+ *   new_slots_d   dev int32 [B]; slots outside [0, C_cold) are not written
+ *   other arguments as gkv_attn_decode (cold_indices_d already holds the
+ *   new slots at the ends of the tables)
+ * Inside the launch the new token's K/V are read from k_new/v_new, so no part
+ * of the step waits for the append, and the workgroups that attend it copy it
+ * into its slot.  Errors as gkv_attn_decode, and GKV_ERR_INVALID (nothing
+ * enqueued) if a pointer is null or misaligned or a request's slot table is
+ * empty.  Asynchronous on `stream`; the plan diagnostics and kernel timing
+ * are those of gkv_attn_decode. */
+int gkv_decode_step(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                    const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
+                    const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
+                    void* stream, int32_t* backend_out);
+
 /* Per-step rule alone (host, no GPU): backend for a batch of `batch` requests
  * under the context's threshold and override (paperlayer.ai §3 "Per-step
  * dispatch": dense iff M_eff = B * n_q/n_kv >= M_sat). */

@@ -341,10 +341,16 @@ int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* 
   return GKV_OK;
 }
 
-int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
-                    const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
-                    const int32_t* cold_indptr_d, const int32_t* cold_indices_d, void* out,
-                    float* lse, void* stream, int32_t* backend_out) {
+}  // extern "C"
+
+namespace {
+
+// The decode step behind gkv_attn_decode (k_new == nullptr) and
+// gkv_decode_step (the batch's new tokens appended inside the launch).
+int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
+                const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
+                void* stream, int32_t* backend_out) {
   if (!ctx) return GKV_ERR_INVALID;
   const auto t_start = std::chrono::steady_clock::now();
   if (int r = check_layer(ctx, layer)) return r;
@@ -357,9 +363,17 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   const bool any_suffix = cold_indptr_h[batch] != cold_indptr_h[0];
   if (any_suffix && !cold_indices_d)
     return fail(ctx, GKV_ERR_INVALID, "attn_decode: slot table pointer is null");
-  (void)cold_indptr_d;
   if (any_suffix && c.cold_capacity_tokens == 0)
     return fail(ctx, GKV_ERR_INVALID, "slot tables given but the COLD pool is empty");
+  if (k_new) {
+    if (!v_new || !new_slots_d) return fail(ctx, GKV_ERR_INVALID, "decode_step: null pointer argument");
+    if (reinterpret_cast<uintptr_t>(k_new) % 16 || reinterpret_cast<uintptr_t>(v_new) % 16)
+      return fail(ctx, GKV_ERR_INVALID, "decode_step: new rows must be 16-byte aligned");
+    for (int32_t b = 0; b < batch; ++b)
+      if (cold_indptr_h[b + 1] <= cold_indptr_h[b])
+        return fail(ctx, GKV_ERR_INVALID, "decode_step: request " + std::to_string(b) +
+                                              " has an empty slot table (its new token must be its last entry)");
+  }
 
   int32_t backend = gkv::choose_backend(batch, group, ctx->m_sat, ctx->force);
   if (backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) {
@@ -403,6 +417,9 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   a.v_cold = L.v_cold;
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
   a.cold_indices = cold_indices_d;
+  a.k_new = k_new;
+  a.v_new = k_new ? v_new : nullptr;
+  a.new_slots = k_new ? new_slots_d : nullptr;
   a.counters = reinterpret_cast<int32_t*>(ws);
   a.p_o = ws + off_po;
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
@@ -435,6 +452,29 @@ int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
   ctx->have_last = true;
   if (backend_out) *backend_out = backend;
   return GKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
+                    const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
+                    const int32_t* cold_indptr_d, const int32_t* cold_indices_d, void* out,
+                    float* lse, void* stream, int32_t* backend_out) {
+  (void)cold_indptr_d;
+  return decode_impl(ctx, layer, q, nullptr, nullptr, nullptr, batch, hot_prefix_ids, cold_indptr_h,
+                     cold_indices_d, out, lse, stream, backend_out);
+}
+
+int gkv_decode_step(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                    const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
+                    const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
+                    void* stream, int32_t* backend_out) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (!k_new) return fail(ctx, GKV_ERR_INVALID, "decode_step: null pointer argument");
+  return decode_impl(ctx, layer, q, k_new, v_new, new_slots_d, batch, hot_prefix_ids, cold_indptr_h,
+                     cold_indices_d, out, lse, stream, backend_out);
 }
 
 }  // extern "C"

@@ -789,6 +789,28 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
     const int n_tiles = (len + kSuffixTile - 1) / kSuffixTile;
     const int cap1 = a.cold_cap - 1;
+    // Fused decode step: the wave whose piece ends the slot table reads the
+    // table's last token (the request's new one) from k_new/v_new, and
+    // copies this KV head's share of it into the new slot (the eight KV-head
+    // workgroups of the part write the whole row; nothing else reads that
+    // slot in the step).  Slots outside the pool are skipped.
+    const bool fresh = a.k_new != nullptr && w1 == tb1;
+    const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
+    const T* knew = static_cast<const T*>(a.k_new) + new_row;
+    const T* vnew = static_cast<const T*>(a.v_new) + new_row + TR::EPB * n;
+    if (fresh) {
+      constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
+      static_assert(CH <= 32, "a row copy takes at most half a wave");
+      const int slot = a.new_slots[b];
+      if (slot >= 0 && slot < a.cold_cap) {
+        const size_t dst = (static_cast<size_t>(slot) * a.n_kv + gk) * D;
+        const int ch = lane & 31;
+        const T* src = static_cast<const T*>(lane < 32 ? a.k_new : a.v_new) + new_row;
+        T* to = static_cast<T*>(const_cast<void*>(lane < 32 ? a.k_cold : a.v_cold)) + dst;
+        if (ch < CH)
+          reinterpret_cast<u32x4*>(to)[ch] = reinterpret_cast<const u32x4*>(src)[ch];
+      }
+    }
 
     // the piece's slot ids, clamped into the pool, staged in this wave's
     // LDS row once: no tile waits on a slot-id load.  The loads of 256 ids
@@ -811,15 +833,28 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
     else TR::zero_row(st.q);
 
-    auto load_kv = [&](int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
+    // kFresh: the table's last token (position len - 1 of this piece) comes
+    // from the new rows (last tile of a fresh wave only)
+    auto load_kv = [&](auto fresh_tag, int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
+      constexpr bool kFresh = decltype(fresh_tag)::value;
       const int base = kSuffixTile * i, last = len - 1;
-      const int s0 = ids[min(base + n, last)], s1 = ids[min(base + 16 + n, last)];
-      TR::load_row(k0, kc + static_cast<size_t>(s0) * stride, g);
-      TR::load_row(k1, kc + static_cast<size_t>(s1) * stride, g);
+      const int i0 = min(base + n, last), i1 = min(base + 16 + n, last);
+      const T* p0 = kc + static_cast<size_t>(ids[i0]) * stride;
+      const T* p1 = kc + static_cast<size_t>(ids[i1]) * stride;
+      if constexpr (kFresh) {
+        if (i0 == last) p0 = knew;
+        if (i1 == last) p1 = knew;
+      }
+      TR::load_row(k0, p0, g);
+      TR::load_row(k1, p1, g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int se = ids[min(base + tau(g, e), last)];
-        v[e] = TR::load_v(vc + static_cast<size_t>(se) * stride);
+        const int ie = min(base + tau(g, e), last);
+        const T* pv = vc + static_cast<size_t>(ids[ie]) * stride;
+        if constexpr (kFresh) {
+          if (ie == last) pv = vnew;
+        }
+        v[e] = TR::load_v(pv);
       }
     };
     auto run_tile = [&](const KOp (&k0)[TR::KS], const KOp (&k1)[TR::KS], const VVec (&v)[8], int i) {
@@ -835,7 +870,8 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     KOp k0[TR::KS], k1[TR::KS];
     VVec v[8];
     for (int i = 0; i < n_tiles; ++i) {
-      load_kv(i, k0, k1, v);
+      if (fresh && i == n_tiles - 1) load_kv(std::true_type{}, i, k0, k1, v);
+      else load_kv(std::false_type{}, i, k0, k1, v);
       run_tile(k0, k1, v, i);
     }
     lse2 = st.finish(o);

@@ -108,6 +108,12 @@ struct StepArgs {
   int32_t cold_cap;
   int32_t pad2_;
   const int32_t* cold_indices; // dev
+  // fused decode step (null otherwise): request b's new token, the last
+  // entry of its slot table, is read from k_new/v_new [B][n_kv][head_dim]
+  // and copied into COLD slot new_slots[b] inside the launch
+  const void* k_new;
+  const void* v_new;
+  const int32_t* new_slots;    // dev [B]
   void* p_o;                   // prefix partials [rows][head_dim], normalised, in the input dtype
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
   void* s_o;                   // suffix-part partials, row = part * n_q + h (input dtype)

@@ -119,3 +119,15 @@ class DecodeState:
     def run(self, out, lse, layer: int = 0, stream=None) -> int:
         return self.ctx.attn_decode(layer, self.q, self.hot_ids, self.indptr_h, self.indptr_d,
                                     self.indices_d, out, lse, stream=stream)
+
+    def last_slots(self) -> np.ndarray:
+        """Slot of each request's last slot-table entry (its decode token)."""
+        if not np.all(np.diff(self.indptr_h) > 0):
+            raise ValueError("a request has an empty slot table")
+        return self.indices_h[self.indptr_h[1:] - 1].astype(np.int32)
+
+    def step(self, out, lse, k_new, v_new, slots_dev, layer: int = 0, stream=None) -> int:
+        """One fused decode step (gkv_decode_step): request b's new token
+        (k_new[b], v_new[b]) goes into slots_dev[b], its last table entry."""
+        return self.ctx.decode_step(layer, self.q, k_new, v_new, slots_dev, self.hot_ids, self.indptr_h,
+                                    self.indices_d, out, lse, stream=stream)

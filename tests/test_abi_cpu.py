@@ -235,6 +235,23 @@ def test_attn_decode_rejects_bad_steps_before_any_device_work():
         c2.attn_decode(0, 16, [pid2], [0, 3], 16, 16, 16, 16, stream=0)
 
 
+def test_decode_step_rejects_bad_steps_before_any_device_work():
+    c = _ctx()
+    pid, _ = c.hot_pool_alloc(10)
+    c.bind_layer(0, 16, 16, 16, 16)   # fake aligned addresses: only host checks run below
+    c.bind_workspace(256, 1 << 20)
+    # layer, q, k_new, v_new, new slots, ids, indptr, indices, out, lse
+    with pytest.raises(binding.GkvError, match="null pointer"):
+        c.decode_step(0, 16, 0, 16, 16, [pid], [0, 1], 16, 16, 16, stream=0)
+    with pytest.raises(binding.GkvError, match="null pointer"):
+        c.decode_step(0, 16, 16, 16, 0, [pid], [0, 1], 16, 16, 16, stream=0)
+    with pytest.raises(binding.GkvError, match="16-byte aligned"):
+        c.decode_step(0, 16, 24, 16, 16, [pid], [0, 1], 16, 16, 16, stream=0)
+    # every request's new token is the last entry of its table: none may be empty
+    with pytest.raises(binding.GkvError, match="empty slot table"):
+        c.decode_step(0, 16, 16, 16, 16, [pid, pid], [0, 1, 1], 16, 16, 16, batch=2, stream=0)
+
+
 def test_workspace_bound_covers_plans():
     c = _ctx(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", hot_capacity_tokens=16384,
              cold_capacity_tokens=65536)

@@ -334,3 +334,79 @@ def test_long_suffixes_span_several_parts(force):
     assert plan["joins_partials"] == 1
     assert plan["n_suffix_parts"] == sum(max(1, -(-n // pt)) for n in (5000, 10, 0, 9000))
     check(out, lse, *oracle_ref(w))
+
+
+# ------------------------------------------------------- fused decode step
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _fused_cases():
+    tiny = workloads.SPECS["tiny"]
+    return {
+        "tiny_f32": (tiny, AUTO, None),
+        "ragged_cascade": (spec(batch=6, fixed_suffix=(1, 31, 32, 33, 257, 700)), CASCADE, None),
+        "ragged_dense": (spec(batch=6, fixed_suffix=(1, 31, 32, 33, 257, 700)), DENSE, None),
+        "group5_d64": (spec(n_q=20, n_kv=4, head_dim=64, batch=5, fixed_suffix=(2, 64, 65, 129, 3)), AUTO, None),
+        "suffix_only_requests": (spec(batch=6, prefix_len=700, fixed_suffix=(10, 1, 40, 1, 300, 64)), AUTO, [2, 4]),
+        "fallback_to_cold": (spec(batch=4, prefix_len=900, fixed_suffix=(3, 50, 129, 400)), AUTO, "cold"),
+        "multi_part": (spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
+                            fixed_suffix=(5000, 10, 1, 9000)), AUTO, None),
+    }
+
+
+@pytest.mark.parametrize("case", list(_fused_cases()))
+def test_fused_step_equals_append_then_attend(case):
+    """gkv_decode_step (append the batch's new tokens and attend, one launch)
+    against gkv_cold_append followed by gkv_attn_decode on an identical
+    placement: out, lse and both COLD pools agree bit for bit.  The new rows
+    are fresh random values, so reading a stale pool row would show."""
+    s, force, variant = _fused_cases()[case]
+    w = workloads.make(s)
+    kw = {}
+    if isinstance(variant, list):
+        w.request_prefix[variant] = -1            # some requests without a HOT prefix
+    elif variant == "cold":
+        kw["hot_capacity"] = 512                  # the prefix falls back to COLD slots
+    sa = DecodeState(w, force_backend=force, **kw)
+    sb = DecodeState(w, force_backend=force, **kw)
+    if variant == "cold":
+        assert all(i == -1 for i in sa.hot_ids)
+    slots = torch.from_numpy(sa.last_slots()).cuda()
+    assert np.array_equal(sa.last_slots(), sb.last_slots())
+    g = torch.Generator().manual_seed(7)
+    shape = (w.batch, w.spec.n_kv, w.spec.head_dim)
+    k_new = torch.randn(shape, generator=g).to(w.torch_dtype).cuda()
+    v_new = torch.randn(shape, generator=g).to(w.torch_dtype).cuda()
+
+    out_a, lse_a = sa.new_outputs()
+    sa.append(0, k_new, v_new, slots)
+    ba = sa.run(out_a, lse_a)
+    out_b, lse_b = sb.new_outputs()
+    bb = sb.step(out_b, lse_b, k_new, v_new, slots)
+    torch.cuda.synchronize()
+    assert ba == bb
+    assert torch.equal(_bits(out_a), _bits(out_b))
+    assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
+    for i in (2, 3):                                  # k_cold, v_cold
+        assert torch.equal(_bits(sa.pools[0][i]), _bits(sb.pools[0][i]))
+    # the appended rows are the new ones
+    assert torch.equal(_bits(sb.pools[0][2][slots.long()]), _bits(k_new))
+    assert torch.equal(_bits(sb.pools[0][3][slots.long()]), _bits(v_new))
+
+
+def test_fused_step_repeats_and_matches_the_oracle():
+    """Repeated fused steps on one state (the pool already holds the new
+    rows from the previous step) stay equal to the oracle."""
+    w = workloads.make(spec(batch=5, fixed_suffix=(7, 70, 700, 1, 33)))
+    st = DecodeState(w)
+    slots = torch.from_numpy(st.last_slots()).cuda()
+    last = torch.from_numpy(w.suffix_offsets[1:] - 1)
+    k_new = w.suffix_k[last].cuda().contiguous()
+    v_new = w.suffix_v[last].cuda().contiguous()
+    ref = oracle_ref(w)
+    for _ in range(3):
+        out, lse = st.new_outputs()
+        st.step(out, lse, k_new, v_new, slots)
+        torch.cuda.synchronize()
+        check(out, lse, *ref)
