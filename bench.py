@@ -154,6 +154,41 @@ def build_state(w, replicas, force):
     return DecodeState(w, n_layers=replicas, force_backend=force)
 
 
+def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
+    """Measured streaming ceilings of this GPU, a second denominator beside the
+    8 TB/s data-sheet peak: the best plain read of n_bytes among a row sum and
+    a matrix-vector product over a [n/8192, 4096] bf16 matrix (both read every
+    byte once; a flat tensor sum reads slower here), and a plain device copy
+    (n_bytes read + n_bytes written); best of `reps` each."""
+    import torch
+    x = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    m = x.view(-1, 4096)
+    vec = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e-3)
+        return min(t)
+
+    reads = {"row_sum": n_bytes / best(lambda: m.sum(dim=1)) / 1e9,
+             "gemv": n_bytes / best(lambda: torch.mv(m, vec)) / 1e9}
+    copy = 2 * n_bytes / best(lambda: y.copy_(x)) / 1e9
+    del x, y, m
+    torch.cuda.empty_cache()
+    how = max(reads, key=reads.get)
+    return {"read_gbps": round(reads[how], 1), "read_kernel": how, "copy_gbps": round(copy, 1),
+            "bytes": n_bytes, "how": "best of %d per kernel over a 1 GiB bf16 buffer" % reps}
+
+
 def step_inputs(w, st):
     """The batch's current tokens: the last slot-table entry of each request
     (all requests have one in the benchmark workloads) and its K/V row
@@ -253,6 +288,9 @@ def run_bench(args):
     if alg["prefix_flops"] > 0:
         roofline["step_kernel_mfma_frac"] = round((alg["prefix_flops"] + alg["suffix_flops"]) /
                                                   (kern_ms["step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    ceiling = stream_ceiling()
+    roofline["stream_read_gbps"] = ceiling["read_gbps"]
+    roofline["frac_of_stream_read"] = round(achieved / ceiling["read_gbps"], 4)
     value = w.batch / (ms_step * 1e-3)
     step_gbps = alg["step_bytes"] / (ms_step * 1e-3) / 1e9
     res = {
@@ -277,6 +315,7 @@ def run_bench(args):
         "step_launches": 2 if args.separate else 1,
         "host_plan_us": round(plan["host_plan_us"], 3),
         "roofline": roofline,
+        "stream_ceiling": ceiling,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on a bounded sample ...")
@@ -344,6 +383,108 @@ def fit_msat(args):
                                            for n in args.fit_workloads.split(",")}}), flush=True)
 
 
+def paged_comparator(args):
+    """The same prefix attention over two storage layouts, at the Llama-3.1-8B
+    attention shape (32q/8kv, d=128, bf16), L_p tokens, B requests each with
+    one current token of its own:
+      hot_slab  the prefix once in a contiguous HOT slab shared by the batch;
+      paged     a per-request copy of the prefix in uniform 16-token pages of
+                the COLD pool (pages in random order), attended through each
+                request's slot table: the prefix bytes are read B times.
+    Times the step kernel of gkv_attn_decode on each (kernel start/end
+    events; the HOT side rotates over 4 layer copies, more than the 256 MB
+    MALL holds) and checks that the two outputs agree."""
+    import torch
+
+    from shared_prefix_paged_contiguous_amd import binding, workloads
+
+    bsz, plen, page = args.cmp_batch, args.cmp_prefix, 16
+    assert plen % page == 0
+    s = workloads.SPECS["llama8b_lp16k_b64"]
+    n_q, n_kv, d = s.n_q, s.n_kv, s.head_dim
+    rng = np.random.default_rng(0)
+
+    def vals(shape):
+        return torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32)).to(torch.bfloat16).cuda()
+
+    q, pk, pv = vals((bsz, n_q, d)), vals((plen, n_kv, d)), vals((plen, n_kv, d))
+    ck, cv = vals((bsz, n_kv, d)), vals((bsz, n_kv, d))     # each request's current token
+    row = n_kv * d * 2
+
+    def timed(ctx, layers, ids, indptr, indices_d, reps=20):
+        out = torch.empty((bsz, n_q, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((bsz, n_q), dtype=torch.float32, device="cuda")
+        run = lambda i: ctx.attn_decode(i % layers, q, ids, indptr, None, indices_d, out, lse)
+        for i in range(3):
+            run(i)
+        ctx.kernel_timing(reps)
+        for i in range(reps):
+            run(i)
+        us = float(ctx.kernel_timing_read(reps).mean()) * 1e3
+        ctx.kernel_timing(0)
+        return us, out, lse
+
+    res = {"mode": "paged_comparator", "batch": bsz, "prefix_tokens": plen, "page_tokens": page,
+           "shape": "32q/8kv d=128 bf16"}
+    # ---- HOT slab shared by the batch
+    layers = 4
+    ctx = binding.Context(n_q, n_kv, d, "bf16", plen, bsz, n_layers=layers)
+    pid, _ = ctx.hot_pool_alloc(plen)
+    hot_elems = ctx.hot_pool_bytes() // 2
+    keep = []
+    for layer in range(layers):
+        k_hot = torch.zeros(hot_elems, dtype=torch.bfloat16, device="cuda")
+        v_hot = torch.zeros_like(k_hot)
+        k_cold = torch.zeros((bsz, n_kv, d), dtype=torch.bfloat16, device="cuda")
+        v_cold = torch.zeros_like(k_cold)
+        ctx.bind_layer(layer, k_hot, v_hot, k_cold, v_cold)
+        ctx.hot_write(layer, pid, 0, pk, pv)
+        ctx.cold_append(layer, ck, cv, torch.arange(bsz, dtype=torch.int32, device="cuda"))
+        keep.append((k_hot, v_hot, k_cold, v_cold))
+    indptr = np.arange(bsz + 1, dtype=np.int32)
+    ws = torch.empty(ctx.workspace_size(bsz, bsz), dtype=torch.uint8, device="cuda")
+    ctx.bind_workspace(ws)
+    us_hot, out_hot, lse_hot = timed(ctx, layers, [pid] * bsz, indptr,
+                                     torch.arange(bsz, dtype=torch.int32, device="cuda"))
+    res["hot_slab"] = {"kernel_us": round(us_hot, 2), "backend": binding.BACKEND_NAMES[ctx.last_plan()["backend"]],
+                       "prefix_bytes_read": 2 * plen * row}
+    out_hot, lse_hot = out_hot.float().cpu(), lse_hot.cpu()
+    del keep, ws, ctx
+    torch.cuda.empty_cache()
+    log(f"[cmp] hot slab: {us_hot:.1f} us")
+
+    # ---- per-request paged copies in COLD
+    cap = bsz * plen + bsz
+    ctx = binding.Context(n_q, n_kv, d, "bf16", 0, cap)
+    k_cold = torch.zeros((cap, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    v_cold = torch.zeros_like(k_cold)
+    ctx.bind_layer(0, None, None, k_cold, v_cold)
+    pages = rng.permutation(bsz * plen // page).astype(np.int64)
+    per = plen // page
+    tables = []
+    for b in range(bsz):
+        slots = (pages[b * per:(b + 1) * per, None] * page + np.arange(page)[None, :]).reshape(-1)
+        sl = torch.from_numpy(slots.astype(np.int32)).cuda()
+        ctx.cold_append(0, pk, pv, sl)
+        tables.append(np.concatenate([slots, [bsz * plen + b]]).astype(np.int32))
+    ctx.cold_append(0, ck, cv, torch.arange(bsz * plen, cap, dtype=torch.int32, device="cuda"))
+    indices = np.concatenate(tables)
+    indptr = np.arange(bsz + 1, dtype=np.int64) * (plen + 1)
+    ws = torch.empty(ctx.workspace_size(bsz, int(indptr[-1])), dtype=torch.uint8, device="cuda")
+    ctx.bind_workspace(ws)
+    us_pg, out_pg, lse_pg = timed(ctx, 1, [-1] * bsz, indptr.astype(np.int32), torch.from_numpy(indices).cuda())
+    res["paged"] = {"kernel_us": round(us_pg, 2), "prefix_bytes_read": bsz * 2 * plen * row}
+    err_o = float((out_pg.float().cpu() - out_hot).abs().max())
+    err_l = float((lse_pg.cpu() - lse_hot).abs().max())
+    res["hot_speedup"] = round(us_pg / us_hot, 2)
+    res["paged_gbps"] = round(res["paged"]["prefix_bytes_read"] / (us_pg * 1e-6) / 1e9, 1)
+    res["max_abs_diff"] = {"out": err_o, "lse": err_l}
+    log(f"[cmp] paged: {us_pg:.1f} us, speedup of the HOT slab {us_pg / us_hot:.1f}x, "
+        f"max |out diff| {err_o:.2e}, |lse diff| {err_l:.2e}")
+    assert err_o <= 2e-2 and err_l <= 2e-2, res["max_abs_diff"]
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,6 +502,10 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--fit-msat", action="store_true")
+    ap.add_argument("--paged-comparator", action="store_true",
+                    help="time the prefix over a shared HOT slab vs per-request 16-token COLD pages")
+    ap.add_argument("--cmp-batch", type=int, default=256)
+    ap.add_argument("--cmp-prefix", type=int, default=16384)
     ap.add_argument("--fit-workloads", default="qwen14b_tp2_lp16k_b128,llama8b_lp16k_b64")
     ap.add_argument("--fit-batches", default="8,16,32,64,128,256,384,512,768")
     args = ap.parse_args()
@@ -375,6 +520,9 @@ def main():
         sys.exit(2)
     if args.fit_msat:
         fit_msat(args)
+        return
+    if args.paged_comparator:
+        paged_comparator(args)
         return
     res = run_bench(args)
     print(json.dumps(res), flush=True)
