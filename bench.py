@@ -288,9 +288,10 @@ def run_bench(args):
     if alg["prefix_flops"] > 0:
         roofline["step_kernel_mfma_frac"] = round((alg["prefix_flops"] + alg["suffix_flops"]) /
                                                   (kern_ms["step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
-    ceiling = stream_ceiling()
-    roofline["stream_read_gbps"] = ceiling["read_gbps"]
-    roofline["frac_of_stream_read"] = round(achieved / ceiling["read_gbps"], 4)
+    ceiling = None if args.no_ceiling else stream_ceiling()
+    if ceiling:
+        roofline["stream_read_gbps"] = ceiling["read_gbps"]
+        roofline["frac_of_stream_read"] = round(achieved / ceiling["read_gbps"], 4)
     value = w.batch / (ms_step * 1e-3)
     step_gbps = alg["step_bytes"] / (ms_step * 1e-3) / 1e9
     res = {
@@ -499,6 +500,8 @@ def main():
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the same-layer pass (profiling: every step kernel then reads from HBM)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-ceiling measurement (profiling runs: keeps its copies out of the counters)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--fit-msat", action="store_true")
