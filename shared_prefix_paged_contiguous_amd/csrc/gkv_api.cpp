@@ -132,9 +132,10 @@ int gkv_create(const gkv_config* cfg, gkv_ctx** out) {
 
 void gkv_destroy(gkv_ctx* ctx) {
   if (!ctx) return;
+  // nothing can be reported from here: release what can be released
   for (hipEvent_t e : ctx->timing_events) {
-    hipEventSynchronize(e);
-    hipEventDestroy(e);
+    (void)hipEventSynchronize(e);
+    (void)hipEventDestroy(e);
   }
   delete ctx;
 }
@@ -305,13 +306,17 @@ int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out) {
 int gkv_kernel_timing(gkv_ctx* ctx, int32_t capacity) {
   if (!ctx) return GKV_ERR_INVALID;
   if (capacity < 0 || capacity > (1 << 20)) return fail(ctx, GKV_ERR_INVALID, "timing capacity out of range");
+  hipError_t first = hipSuccess;
   for (hipEvent_t e : ctx->timing_events) {
-    hipEventSynchronize(e);
-    hipEventDestroy(e);
+    hipError_t r = hipEventSynchronize(e);
+    if (first == hipSuccess) first = r;
+    r = hipEventDestroy(e);
+    if (first == hipSuccess) first = r;
   }
   ctx->timing_events.clear();
   ctx->timing_capacity = 0;
   ctx->timing_used = 0;
+  if (first != hipSuccess) return device_fail(ctx, "releasing timing events", first);
   for (int32_t i = 0; i < 2 * capacity; ++i) {
     hipEvent_t e;
     hipError_t r = hipEventCreate(&e);
