@@ -276,6 +276,9 @@ def run_bench(args):
     per = ctx.kernel_timing_read(args.steps)
     ctx.kernel_timing(0)
     kern_ms = {"step": float(per.mean())}
+    kern_stats = {"mean": round(float(per.mean()) * 1e3, 2), "median": round(float(np.median(per)) * 1e3, 2),
+                  "min": round(float(per.min()) * 1e3, 2), "max": round(float(per.max()) * 1e3, 2),
+                  "calls": int(per.size)}
     log(f"[bench] kernel avg us: " + ", ".join(f"{k}={v*1e3:.1f}" for k, v in kern_ms.items()))
 
     dom = max(kern_ms, key=kern_ms.get)
@@ -309,6 +312,7 @@ def run_bench(args):
         "step_bytes": alg["step_bytes"],
         "warm_ms_per_step": round(ms_warm, 5) if ms_warm is not None else None,
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
+        "kernel_us_stats": kern_stats,
         "kernel_note": ("step = the step kernel of gkv_attn_decode (prefix splits, suffix parts, join); "
                         "gkv_cold_append is a launch of its own" if args.separate else
                         "step = the one launch of gkv_decode_step: new tokens appended, prefix splits, "
