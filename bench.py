@@ -87,14 +87,31 @@ def estimate_step_bytes(w):
 KERNEL_SOURCES = ("kernels.hip", "kernels.h", "plan_types.h")
 
 
+def _code_tokens(src: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so
+    that edits to comments alone leave the hash below unchanged."""
+    import re
+    tok = re.compile(r'"(?:\\.|[^"\\])*"|//[^\n]*|/\*.*?\*/|\s+|.', re.S)
+    out = []
+    for m in tok.finditer(src):
+        t = m.group(0)
+        if t.startswith("//") or t.startswith("/*"):
+            out.append(" ")
+        elif t.isspace():
+            out.append("\n" if "\n" in t else " ")
+        else:
+            out.append(t)
+    return re.sub(r"\s*\n\s*", "\n", re.sub(r"[ ]+", " ", "".join(out))).strip()
+
+
 def kernel_source_sha() -> str:
-    """sha256 over the device-code sources: identifies the kernels a set of
-    hardware counters was taken on."""
+    """sha256 over the code (comments excluded) of the device sources:
+    identifies the kernels a set of hardware counters was taken on."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "shared_prefix_paged_contiguous_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "shared_prefix_paged_contiguous_amd", "csrc", f)) as fh:
+            h.update(_code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

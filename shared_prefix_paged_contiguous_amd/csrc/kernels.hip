@@ -729,7 +729,7 @@ __device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, i
 // the online softmax over its quarter of the part through the slot table and
 // the four results meet in LDS.  A request without a HOT prefix whose slot
 // table is one part is finished here; otherwise the part's partial is written
-// for the merge kernel.
+// for the request's join workgroup.
 template <typename T, int D>
 struct SuffixSmem {
   int32_t ids[kWaves][kWaveTokens];
