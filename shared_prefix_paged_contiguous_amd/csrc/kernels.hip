@@ -748,7 +748,8 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   auto& lds_o = sm.o;
   auto& lds_lse = sm.lse;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: so are the loop bounds
   const int part = blk / a.n_kv;
   const int gk = blk - part * a.n_kv;
   if (part >= a.n_parts) return;   // grid padding
@@ -824,6 +825,9 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       for (int ck = 0; ck < 4; ++ck)
         if (base + 64 * ck + lane < len) ids[base + 64 * ck + lane] = min(max(raw[ck], 0), cap1);
     }
+    // a fresh wave's last position is the new token: id -1 sends its loads to
+    // k_new / v_new (the same wave wrote the position above, in order)
+    if (fresh && lane == 0) ids[len - 1] = -1;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -833,29 +837,21 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
     else TR::zero_row(st.q);
 
-    // kFresh: the table's last token (position len - 1 of this piece) comes
-    // from the new rows (last tile of a fresh wave only)
-    auto load_kv = [&](auto fresh_tag, int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
-      constexpr bool kFresh = decltype(fresh_tag)::value;
+    // Slot id -1 (the new token) reads k_new / v_new.  One branch-free load
+    // sequence serves every tile: with a separate sequence for the fresh
+    // tile the compiler merged the two, and a V load common to both then sank
+    // below the QK^T of the tile, which waits for K, so each tile cost two
+    // memory round trips.
+    auto row = [&](const T* pool, const T* fresh_row, int id) {
+      const T* p = pool + static_cast<size_t>(max(id, 0)) * stride;
+      return id < 0 ? fresh_row : p;
+    };
+    auto load_kv = [&](int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
       const int base = kSuffixTile * i, last = len - 1;
-      const int i0 = min(base + n, last), i1 = min(base + 16 + n, last);
-      const T* p0 = kc + static_cast<size_t>(ids[i0]) * stride;
-      const T* p1 = kc + static_cast<size_t>(ids[i1]) * stride;
-      if constexpr (kFresh) {
-        if (i0 == last) p0 = knew;
-        if (i1 == last) p1 = knew;
-      }
-      TR::load_row(k0, p0, g);
-      TR::load_row(k1, p1, g);
+      TR::load_row(k0, row(kc, knew, ids[min(base + n, last)]), g);
+      TR::load_row(k1, row(kc, knew, ids[min(base + 16 + n, last)]), g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ie = min(base + tau(g, e), last);
-        const T* pv = vc + static_cast<size_t>(ids[ie]) * stride;
-        if constexpr (kFresh) {
-          if (ie == last) pv = vnew;
-        }
-        v[e] = TR::load_v(pv);
-      }
+      for (int e = 0; e < 8; ++e) v[e] = TR::load_v(row(vc, vnew, ids[min(base + tau(g, e), last)]));
     };
     auto run_tile = [&](const KOp (&k0)[TR::KS], const KOp (&k1)[TR::KS], const VVec (&v)[8], int i) {
       typename TR::VOp vo;
@@ -863,16 +859,46 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
       st.tile(k0, k1, vo, min(kSuffixTile, len - kSuffixTile * i), g, c);
     };
 
-    // one tile at a time: the loads of a tile are in flight only while
-    // the wave waits for them, and the other waves of the CU fill the time
-    // (measured: two alternating register sets gained nothing and cost 64
-    // registers)
-    KOp k0[TR::KS], k1[TR::KS];
-    VVec v[8];
-    for (int i = 0; i < n_tiles; ++i) {
-      if (fresh && i == n_tiles - 1) load_kv(std::true_type{}, i, k0, k1, v);
-      else load_kv(std::false_type{}, i, k0, k1, v);
-      run_tile(k0, k1, v, i);
+    // bf16: two register sets, so tile i + 1's loads are in flight while
+    // tile i is computed.  Every load sits outside any branch (the loop is
+    // peeled), so each tile waits only for its own loads, never for the
+    // younger set.  fp32 operands are twice the registers: one set.
+    KOp ka0[TR::KS], ka1[TR::KS];
+    VVec va[8];
+    load_kv(0, ka0, ka1, va);
+    int i = 0;
+    if constexpr (sizeof(T) == 2) {
+      KOp kb0[TR::KS], kb1[TR::KS];
+      VVec vb[8];
+      for (; i + 2 < n_tiles; i += 2) {
+        load_kv(i + 1, kb0, kb1, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        run_tile(ka0, ka1, va, i);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kv(i + 2, ka0, ka1, va);
+        __builtin_amdgcn_sched_barrier(0);
+        run_tile(kb0, kb1, vb, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i + 1 < n_tiles) {
+        load_kv(i + 1, kb0, kb1, vb);
+        __builtin_amdgcn_sched_barrier(0);
+        run_tile(ka0, ka1, va, i);
+        __builtin_amdgcn_sched_barrier(0);
+        run_tile(kb0, kb1, vb, i + 1);
+        i = n_tiles;
+      }
+    } else {
+      for (; i + 1 < n_tiles; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        run_tile(ka0, ka1, va, i);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kv(i + 1, ka0, ka1, va);
+      }
+    }
+    if (i < n_tiles) {
+      __builtin_amdgcn_sched_barrier(0);
+      run_tile(ka0, ka1, va, i);
     }
     lse2 = st.finish(o);
   }
