@@ -518,6 +518,30 @@ __device__ __forceinline__ void load_partial_vals(const T* src, float (&v)[PER])
 // all of this wave's partial stores have completed
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// One 16-byte piece of a partial row with the coherence of the agent-scope
+// stores above (sc1: written through to where every XCD reads it).  A
+// 64-bit address, so partial buffers of any size; the explicit wait in
+// wait_stores() covers it.
+__device__ __forceinline__ void store_chunk(void* dst, const u32x4& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+}
+// 16 bytes of a row from 16 / sizeof(T) floats (LDS), in the dtype T
+template <typename T>
+__device__ __forceinline__ u32x4 pack_chunk(const float* src) {
+  if constexpr (sizeof(T) == 2) {
+    const f32x4 x0 = reinterpret_cast<const f32x4*>(src)[0], x1 = reinterpret_cast<const f32x4*>(src)[1];
+    auto two = [](float lo, float hi) {
+      return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo))) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi))) << 16);
+    };
+    return u32x4{two(x0[0], x0[1]), two(x0[2], x0[3]), two(x1[0], x1[1]), two(x1[2], x1[3])};
+  } else {
+    // the whole vector at once (a bit_cast of one element of an ext_vector
+    // lvalue reads element 0 with this compiler)
+    return __builtin_bit_cast(u32x4, reinterpret_cast<const f32x4*>(src)[0]);
+  }
+}
+
 
 // Joins the partial softmax results of one query head: np parts, part p has
 // base-2 lse lse_of(p) and normalised output row whose PER elements at
@@ -1297,20 +1321,25 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // all 16 rows leave LDS before the first store (one LDS wait, not 16)
-      constexpr int PER = D / 64;
-      float v[16][PER];
+      // 16-byte stores: lane l writes chunk l % CH of row l / CH of each
+      // group of RPI rows, so one instruction covers RPI whole rows.  All
+      // chunks leave LDS before the first store (one LDS wait).
+      constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;
+      constexpr int RPI = 64 / CH;
+      static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
+      const int ch = lane % CH, rsub = lane / CH;
+      u32x4 pk[16 / RPI];
+      int prow_of[16 / RPI];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-#pragma unroll
-        for (int j = 0; j < PER; ++j) v[i][j] = stage[i * kStride + PER * lane + j];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (wrow0 + 16 * rb + i < rows) {
-          const size_t row = static_cast<uint32_t>(__builtin_amdgcn_readlane(prow, i));
-          store_partial_vals<T, PER>(static_cast<T*>(a.p_o) + row * D + PER * lane, v[i]);
-        }
+      for (int s = 0; s < 16 / RPI; ++s) {
+        const int rr = s * RPI + rsub;
+        pk[s] = pack_chunk<T>(stage + rr * kStride + (16 / sizeof(T)) * ch);
+        prow_of[s] = __shfl(prow, rr);
       }
+#pragma unroll
+      for (int s = 0; s < 16 / RPI; ++s)
+        if (wrow0 + 16 * rb + s * RPI + rsub < rows)
+          store_chunk(static_cast<T*>(a.p_o) + static_cast<size_t>(prow_of[s]) * D + (16 / sizeof(T)) * ch, pk[s]);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
