@@ -22,13 +22,19 @@ attention  softmax attention over prefix || suffix, and the log-sum-exp merge
 alloc      HOT first-fit extent allocator model and COLD LIFO free-list model
 append     scatter model of appending new K/V rows into COLD slots
 dispatch   the per-step backend rule M_eff >= M_sat
+registry   the shared-prefix registry: HOT-first admission, COLD fallback, no
+           demotion, cached prefixes evicted least recently released first,
+           and the f_p partition of a KV budget
 
-Pins (see tests/test_oracle_pins.py): closed forms, a pure-Python brute force,
-torch CPU float64 scaled_dot_product_attention, the merge invariant, and
-hand-derived allocator traces.  Every public function here is pinned.
+Pins (tests/test_oracle_pins.py, tests/test_oracle_alloc_pins.py,
+tests/test_oracle_registry_pins.py): closed forms, a pure-Python brute force,
+torch CPU float64 scaled_dot_product_attention, the merge invariant,
+hand-derived allocator and registry traces, and invariants restated by brute
+force.  Every public function here is pinned.
 """
 
 from .attention import attend, decode_step, merge, softmax_scale  # noqa: F401
 from .alloc import ColdAllocModel, HotAllocModel, NoSpace, NotFound  # noqa: F401
 from .append import append_model  # noqa: F401
 from .dispatch import BACKEND_CASCADE, BACKEND_DENSE, choose_backend, m_eff  # noqa: F401
+from .registry import COLD, HOT, InvalidArg, RegistryModel, partition  # noqa: F401
