@@ -507,6 +507,66 @@ def paged_comparator(args):
     print(json.dumps(res), flush=True)
 
 
+def llama8b_kv_budget_tokens() -> int:
+    """KV tokens one MI355X holds for Llama-3.1-8B: 90% of 288 GB of HBM minus
+    the bf16 weights (8.03 B parameters), at 32 layers x 8 KV heads x 128 x
+    2 (K, V) x 2 bytes = 128 KiB per token."""
+    return (int(0.9 * 288e9) - 2 * 8_030_000_000) // (32 * 8 * 128 * 2 * 2)
+
+
+def multi_prefix(args):
+    """Uniform-length multi-prefix sweep (paperlayer.ai Appendix B.8: k in
+    {1, 4, 16, 64} distinct prefixes of 8K tokens, B = 256, Llama-3.1-8B
+    attention shape).  The per-layer KV budget of one MI355X is split with
+    f_p (gkv_partition_capacity); every request takes a reference to its
+    prefix through the registry (gkv_prefix_acquire, request order), so
+    prefixes beyond the HOT pool's room land in COLD and their requests read
+    them through their slot tables.  Times the step kernel per k."""
+    import torch
+
+    from shared_prefix_paged_contiguous_amd import binding, workloads
+    from shared_prefix_paged_contiguous_amd.harness import DecodeState
+
+    total = args.mp_budget_tokens or llama8b_kv_budget_tokens()
+    hot_cap, cold_cap = binding.partition_capacity(total, args.mp_fp)
+    res = {"mode": "multi_prefix", "kv_budget_tokens": total, "f_p": args.mp_fp, "hot_capacity": hot_cap,
+           "cold_capacity": cold_cap, "prefix_tokens": args.mp_prefix, "batch": args.mp_batch,
+           "shape": "32q/8kv d=128 bf16", "suffixes": "U{128..1024}", "rows": []}
+    for k in [int(x) for x in args.mp_ks.split(",")]:
+        t0 = time.perf_counter()
+        w = workloads.make_uniform_multi_prefix(k, prefix_len=args.mp_prefix, batch=args.mp_batch,
+                                                hot_capacity=hot_cap, cold_capacity=cold_cap, device="cuda")
+        replicas = max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
+        st = DecodeState(w, n_layers=replicas, registry=True)
+        alg = algorithmic(w, st)
+        out, lse = st.new_outputs()
+        for i in range(5):
+            st.run(out, lse, layer=i % replicas)
+        steps = args.mp_steps
+        st.ctx.kernel_timing(steps)
+        for i in range(steps):
+            st.run(out, lse, layer=i % replicas)
+        ms = st.ctx.kernel_timing_read(steps)
+        st.ctx.kernel_timing(0)
+        us = float(np.median(ms)) * 1e3
+        rs = st.ctx.registry_stats()
+        plan = st.ctx.last_plan()
+        row = {"k": k, "hot_prefixes": rs["resident_hot"], "cold_prefixes": rs["resident_cold"],
+               "requests_on_cold_prefixes": int(sum(1 for b in range(w.batch)
+                                                    if st.placement["prefix_id"][int(w.request_prefix[b])] < 0)),
+               "backend": binding.BACKEND_NAMES[plan["backend"]], "n_classes": plan["n_classes"],
+               "kernel_us_median": round(us, 1), "kernel_us_min": round(float(ms.min()) * 1e3, 1),
+               "query_tokens_per_s": round(w.batch / (us * 1e-6)),
+               "kernel_bytes": alg["kernel_bytes"]["step"],
+               "achieved_gbps": round(alg["kernel_bytes"]["step"] / (us * 1e-6) / 1e9, 1),
+               "replicas": replicas, "setup_s": round(time.perf_counter() - t0, 1)}
+        res["rows"].append(row)
+        log(f"[multi-prefix] k={k}: {row}")
+        del st, w, out, lse
+        torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -530,6 +590,15 @@ def main():
                     help="time the prefix over a shared HOT slab vs per-request 16-token COLD pages")
     ap.add_argument("--cmp-batch", type=int, default=256)
     ap.add_argument("--cmp-prefix", type=int, default=16384)
+    ap.add_argument("--multi-prefix", action="store_true",
+                    help="uniform multi-prefix sweep through the prefix registry (k prefixes of 8K, B=256)")
+    ap.add_argument("--mp-ks", default="1,4,16,64")
+    ap.add_argument("--mp-prefix", type=int, default=8192)
+    ap.add_argument("--mp-batch", type=int, default=256)
+    ap.add_argument("--mp-fp", type=float, default=0.2)
+    ap.add_argument("--mp-budget-tokens", type=int, default=0,
+                    help="per-layer KV budget in tokens (0: what one MI355X holds for Llama-3.1-8B)")
+    ap.add_argument("--mp-steps", type=int, default=20)
     ap.add_argument("--fit-workloads", default="qwen14b_tp2_lp16k_b128,llama8b_lp16k_b64")
     ap.add_argument("--fit-batches", default="8,16,32,64,128,256,384,512,768")
     args = ap.parse_args()
@@ -547,6 +616,9 @@ def main():
         return
     if args.paged_comparator:
         paged_comparator(args)
+        return
+    if args.multi_prefix:
+        multi_prefix(args)
         return
     res = run_bench(args)
     print(json.dumps(res), flush=True)

@@ -159,6 +159,86 @@ int gkv_cold_pool_free(gkv_ctx* ctx, const int32_t* slots, int32_t n);
 
 int gkv_pool_stats(const gkv_ctx* ctx, gkv_stats* out);
 
+/* ---------------------------------------------------------------- prefixes
+ * Shared-prefix registry: reference-counted prefixes and the admission policy
+ * of the two pools (paperlayer.ai Appendix B.10 "Cross-pool admission and
+ * promotion policy": HOT first, COLD when no contiguous HOT extent fits the
+ * prefix - a full pool or only shorter fragments - and prefixes in HOT are
+ * never demoted; Appendix B.8: every distinct prefix gets a slab of its own;
+ * §1 "Design": admission and eviction are part of the engine).
+ *
+ * A prefix is named by a caller key (e.g. a hash of its tokens).  A prefix
+ * whose last reference is released stays resident as a cached prefix; cached
+ * prefixes are evicted least recently released first, only when an admission
+ * needs their space or on request.  Evicting frees a prefix's slab or slots;
+ * referenced prefixes never move or change pool.  Host-only calls, no GPU.
+ * Slabs and slots owned by the registry are refused by gkv_hot_pool_free and
+ * gkv_cold_pool_free (GKV_ERR_INVALID). */
+
+/* HOT and COLD token capacities for a KV budget of total_tokens tokens per
+ * layer, the HOT pool taking the fraction f_p, fixed at start-up (paperlayer.ai
+ * "Limitations": static HOT/COLD pool fraction, 0.2 by default), rounded down
+ * to whole 32-token blocks: hot = floor(floor(f_p * total) / 32) * 32, cold =
+ * total - hot.  GKV_ERR_INVALID if total < 0, f_p is outside [0, 1] or cold
+ * exceeds 2^31 - 1 slots.  Needs no context. */
+int gkv_partition_capacity(int64_t total_tokens, double f_p, int64_t* hot_tokens,
+                           int64_t* cold_tokens);
+
+enum { GKV_POOL_HOT = 0, GKV_POOL_COLD = 1 };
+
+typedef struct {
+  int32_t pool;         /* GKV_POOL_HOT or GKV_POOL_COLD */
+  int32_t prefix_id;    /* HOT: the slab's prefix id (for hot_prefix_ids); COLD: -1 */
+  int64_t hot_offset;   /* HOT: token offset of the slab; COLD: -1 */
+  int32_t n_tokens;     /* prefix length */
+  int32_t fresh;        /* 1 if this call admitted the prefix: the caller writes its
+                           K/V (gkv_hot_write, or gkv_cold_append on its slots) */
+  int32_t refs;         /* references held after the call */
+  int32_t reserved;
+} gkv_prefix_ref;
+
+/* Take a reference to prefix `key` of n_tokens tokens.  If it is resident the
+ * reference count grows and its placement is returned (fresh = 0; n_tokens
+ * must equal its length, else GKV_ERR_INVALID).  Otherwise it is admitted:
+ *   1. HOT, if a free extent fits it, or if evicting cached HOT prefixes in
+ *      eviction order makes one appear (the fewest such are evicted); the
+ *      slab is placed first-fit as by gkv_hot_pool_alloc;
+ *   2. else COLD, if the free slots - plus those of cached COLD prefixes,
+ *      evicted in order as needed - number n_tokens; popped as by
+ *      gkv_cold_pool_alloc (read them with gkv_prefix_cold_slots);
+ *   3. else GKV_ERR_NOSPACE with nothing changed (no eviction).
+ * out: host, written on success. */
+int gkv_prefix_acquire(gkv_ctx* ctx, uint64_t key, int32_t n_tokens, gkv_prefix_ref* out);
+/* Placement of a resident prefix without changing its count (fresh = 0);
+ * GKV_ERR_NOTFOUND if not resident. */
+int gkv_prefix_lookup(const gkv_ctx* ctx, uint64_t key, gkv_prefix_ref* out);
+/* The COLD slots (host, >= n_tokens entries) of a COLD-resident prefix, in
+ * context order.  GKV_ERR_NOTFOUND if not resident, GKV_ERR_INVALID if it is
+ * in HOT or max_slots < n_tokens. */
+int gkv_prefix_cold_slots(const gkv_ctx* ctx, uint64_t key, int32_t* slots_out, int32_t max_slots);
+/* Drop one reference; at zero the prefix is cached (still resident).
+ * GKV_ERR_NOTFOUND if not resident, GKV_ERR_INVALID if it holds no reference. */
+int gkv_prefix_release(gkv_ctx* ctx, uint64_t key);
+/* Evict a cached prefix now.  GKV_ERR_NOTFOUND if not resident,
+ * GKV_ERR_INVALID if it is referenced. */
+int gkv_prefix_evict(gkv_ctx* ctx, uint64_t key);
+/* Evict cached COLD prefixes, in eviction order, until at least n_free_slots
+ * COLD slots are free (e.g. before allocating a batch's suffix slots).
+ * GKV_ERR_NOSPACE with nothing changed if even all of them would not do. */
+int gkv_prefix_reclaim_cold(gkv_ctx* ctx, int32_t n_free_slots);
+
+typedef struct {
+  int32_t resident_hot;    /* resident prefixes in HOT */
+  int32_t resident_cold;   /* resident prefixes in COLD */
+  int32_t referenced;      /* resident with refs > 0 */
+  int32_t cached;          /* resident with refs == 0 */
+  int64_t hits;            /* acquires of a resident prefix, since create */
+  int64_t hot_admits;      /* admissions to HOT */
+  int64_t cold_admits;     /* admissions to COLD (HOT could not hold the prefix) */
+  int64_t evictions;       /* cached prefixes evicted */
+} gkv_registry_counts;
+int gkv_registry_stats(const gkv_ctx* ctx, gkv_registry_counts* out);
+
 /* Append decoded tokens into COLD (paperlayer.ai §1 "Design": COLD holds
  * suffix and decoded tokens).  k_new, v_new: dev [n][n_kv][head_dim];
  * slots_dev: dev int32 [n].  Row slots[i] of layer `layer`'s k_cold/v_cold

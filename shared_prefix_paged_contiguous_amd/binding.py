@@ -60,6 +60,20 @@ class _PlanInfo(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
 
 
+class _PrefixRef(ctypes.Structure):
+    _fields_ = [("pool", ctypes.c_int32), ("prefix_id", ctypes.c_int32), ("hot_offset", ctypes.c_int64),
+                ("n_tokens", ctypes.c_int32), ("fresh", ctypes.c_int32), ("refs", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class _RegistryCounts(ctypes.Structure):
+    _fields_ = [("resident_hot", ctypes.c_int32), ("resident_cold", ctypes.c_int32),
+                ("referenced", ctypes.c_int32), ("cached", ctypes.c_int32), ("hits", ctypes.c_int64),
+                ("hot_admits", ctypes.c_int64), ("cold_admits", ctypes.c_int64), ("evictions", ctypes.c_int64)]
+
+
+POOL_HOT, POOL_COLD = 0, 1
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -82,6 +96,14 @@ SIGNATURES = {
     "gkv_cold_pool_alloc": (ctypes.c_int, [_P, _I32, _PI32]),
     "gkv_cold_pool_free": (ctypes.c_int, [_P, _PI32, _I32]),
     "gkv_pool_stats": (ctypes.c_int, [_P, ctypes.POINTER(_Stats)]),
+    "gkv_partition_capacity": (ctypes.c_int, [_I64, ctypes.c_double, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "gkv_prefix_acquire": (ctypes.c_int, [_P, ctypes.c_uint64, _I32, ctypes.POINTER(_PrefixRef)]),
+    "gkv_prefix_lookup": (ctypes.c_int, [_P, ctypes.c_uint64, ctypes.POINTER(_PrefixRef)]),
+    "gkv_prefix_cold_slots": (ctypes.c_int, [_P, ctypes.c_uint64, _PI32, _I32]),
+    "gkv_prefix_release": (ctypes.c_int, [_P, ctypes.c_uint64]),
+    "gkv_prefix_evict": (ctypes.c_int, [_P, ctypes.c_uint64]),
+    "gkv_prefix_reclaim_cold": (ctypes.c_int, [_P, _I32]),
+    "gkv_registry_stats": (ctypes.c_int, [_P, ctypes.POINTER(_RegistryCounts)]),
     "gkv_cold_append": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "gkv_attn_decode": (ctypes.c_int, [_P, _I32, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P, _P]),
     "gkv_decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P]),
@@ -110,6 +132,16 @@ def load_library(path: str = LIB_PATH):
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def partition_capacity(total_tokens: int, f_p: float = 0.2):
+    """gkv_partition_capacity: (hot, cold) token capacities of a KV budget."""
+    lib = load_library()
+    hot, cold = _I64(), _I64()
+    rc = lib.gkv_partition_capacity(total_tokens, f_p, ctypes.byref(hot), ctypes.byref(cold))
+    if rc != GKV_OK:
+        raise GkvError(rc, "partition_capacity: total < 0, f_p outside [0, 1] or COLD above 2^31 - 1 slots")
+    return hot.value, cold.value
 
 
 def _ptr(x) -> Optional[int]:
@@ -201,6 +233,37 @@ class Context:
         st = _Stats()
         self._check(self._lib.gkv_pool_stats(self._h, ctypes.byref(st)), "pool_stats")
         return {f: getattr(st, f) for f, _ in _Stats._fields_}
+
+    # ------------------------------------------------------------- prefixes
+    def prefix_acquire(self, key: int, n_tokens: int) -> dict:
+        r = _PrefixRef()
+        self._check(self._lib.gkv_prefix_acquire(self._h, key, n_tokens, ctypes.byref(r)), "prefix_acquire")
+        return {f: getattr(r, f) for f, _ in _PrefixRef._fields_ if f != "reserved"}
+
+    def prefix_lookup(self, key: int) -> dict:
+        r = _PrefixRef()
+        self._check(self._lib.gkv_prefix_lookup(self._h, key, ctypes.byref(r)), "prefix_lookup")
+        return {f: getattr(r, f) for f, _ in _PrefixRef._fields_ if f != "reserved"}
+
+    def prefix_cold_slots(self, key: int, n_tokens: int) -> np.ndarray:
+        out = np.empty(n_tokens, dtype=np.int32)
+        self._check(self._lib.gkv_prefix_cold_slots(self._h, key, out.ctypes.data_as(_PI32), n_tokens),
+                    "prefix_cold_slots")
+        return out
+
+    def prefix_release(self, key: int):
+        self._check(self._lib.gkv_prefix_release(self._h, key), "prefix_release")
+
+    def prefix_evict(self, key: int):
+        self._check(self._lib.gkv_prefix_evict(self._h, key), "prefix_evict")
+
+    def prefix_reclaim_cold(self, n_free_slots: int):
+        self._check(self._lib.gkv_prefix_reclaim_cold(self._h, n_free_slots), "prefix_reclaim_cold")
+
+    def registry_stats(self) -> dict:
+        c = _RegistryCounts()
+        self._check(self._lib.gkv_registry_stats(self._h, ctypes.byref(c)), "registry_stats")
+        return {f: getattr(c, f) for f, _ in _RegistryCounts._fields_}
 
     # --------------------------------------------------------------- memory
     def bind_layer(self, layer: int, k_hot, v_hot, k_cold, v_cold):

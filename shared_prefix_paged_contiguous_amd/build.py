@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgkv.so")
-SOURCES = ["kernels.hip", "gkv_api.cpp", "plan.cpp", "pools.cpp"]
+SOURCES = ["kernels.hip", "gkv_api.cpp", "plan.cpp", "pools.cpp", "registry.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -16,6 +16,7 @@
 #include "kernels.h"
 #include "plan.h"
 #include "pools.h"
+#include "registry.h"
 
 namespace {
 
@@ -45,6 +46,7 @@ struct gkv_ctx {
   gkv_config cfg;
   gkv::HotPool hot;
   gkv::ColdPool cold;
+  gkv::Registry reg;   // owns the prefixes admitted through gkv_prefix_acquire
   std::vector<Layer> layers;
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -63,6 +65,7 @@ struct gkv_ctx {
       : cfg(c),
         hot(c.hot_capacity_tokens, gkv::kHotBlock),
         cold(static_cast<int32_t>(c.cold_capacity_tokens)),
+        reg(hot, cold),
         layers(c.n_layers),
         m_sat(c.m_sat > 0 ? c.m_sat : kDefaultMSat),
         force(c.force_backend) {}
@@ -220,6 +223,9 @@ int gkv_hot_pool_alloc(gkv_ctx* ctx, int32_t n_tokens, int32_t* prefix_id, int64
 
 int gkv_hot_pool_free(gkv_ctx* ctx, int32_t prefix_id) {
   if (!ctx) return GKV_ERR_INVALID;
+  if (ctx->reg.owns_hot(prefix_id))
+    return fail(ctx, GKV_ERR_INVALID, "prefix id " + std::to_string(prefix_id) +
+                                          " belongs to the prefix registry (gkv_prefix_release / gkv_prefix_evict)");
   if (ctx->hot.release(prefix_id) != 0)
     return fail(ctx, GKV_ERR_NOTFOUND, "prefix id " + std::to_string(prefix_id) + " is not live");
   return GKV_OK;
@@ -242,6 +248,10 @@ int gkv_cold_pool_alloc(gkv_ctx* ctx, int32_t n, int32_t* slots_out) {
 int gkv_cold_pool_free(gkv_ctx* ctx, const int32_t* slots, int32_t n) {
   if (!ctx) return GKV_ERR_INVALID;
   if (n < 0 || (n > 0 && !slots)) return fail(ctx, GKV_ERR_INVALID, "cold_pool_free: bad arguments");
+  for (int32_t i = 0; i < n; ++i)
+    if (ctx->reg.owns_cold_slot(slots[i]))
+      return fail(ctx, GKV_ERR_INVALID, "cold_pool_free: slot " + std::to_string(slots[i]) +
+                                            " belongs to a registry prefix (gkv_prefix_release / gkv_prefix_evict)");
   if (ctx->cold.release(slots, n) != 0)
     return fail(ctx, GKV_ERR_NOTFOUND, "cold_pool_free: a slot is out of range, not allocated or repeated");
   return GKV_OK;
@@ -254,6 +264,84 @@ int gkv_pool_stats(const gkv_ctx* ctx, gkv_stats* out) {
   out->hot_live_prefixes = ctx->hot.live_count();
   out->hot_free_extents = ctx->hot.extent_count();
   out->cold_free_slots = ctx->cold.free_count();
+  return GKV_OK;
+}
+
+int gkv_partition_capacity(int64_t total_tokens, double f_p, int64_t* hot_tokens, int64_t* cold_tokens) {
+  if (!hot_tokens || !cold_tokens || total_tokens < 0 || !(f_p >= 0.0 && f_p <= 1.0)) return GKV_ERR_INVALID;
+  const int64_t hot = static_cast<int64_t>(f_p * static_cast<double>(total_tokens)) / gkv::kHotBlock * gkv::kHotBlock;
+  const int64_t cold = total_tokens - hot;
+  if (cold > 0x7fffffffLL || hot > (1LL << 40)) return GKV_ERR_INVALID;
+  *hot_tokens = hot;
+  *cold_tokens = cold;
+  return GKV_OK;
+}
+
+namespace {
+void fill_ref(const gkv::PrefixEntry& e, bool fresh, gkv_prefix_ref* out) {
+  out->pool = e.pool == 0 ? GKV_POOL_HOT : GKV_POOL_COLD;
+  out->prefix_id = e.pool == 0 ? e.hot_id : -1;
+  out->hot_offset = e.pool == 0 ? e.offset : -1;
+  out->n_tokens = e.n;
+  out->fresh = fresh ? 1 : 0;
+  out->refs = e.refs;
+  out->reserved = 0;
+}
+}  // namespace
+
+int gkv_prefix_acquire(gkv_ctx* ctx, uint64_t key, int32_t n_tokens, gkv_prefix_ref* out) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (!out) return fail(ctx, GKV_ERR_INVALID, "prefix_acquire: out is null");
+  const gkv::PrefixEntry* e = nullptr;
+  bool fresh = false;
+  if (int r = ctx->reg.acquire(key, n_tokens, &e, &fresh, ctx->err)) return r;
+  fill_ref(*e, fresh, out);
+  return GKV_OK;
+}
+
+int gkv_prefix_lookup(const gkv_ctx* ctx, uint64_t key, gkv_prefix_ref* out) {
+  if (!ctx || !out) return GKV_ERR_INVALID;
+  const gkv::PrefixEntry* e = ctx->reg.find(key);
+  if (!e) return GKV_ERR_NOTFOUND;
+  fill_ref(*e, false, out);
+  return GKV_OK;
+}
+
+int gkv_prefix_cold_slots(const gkv_ctx* ctx, uint64_t key, int32_t* slots_out, int32_t max_slots) {
+  if (!ctx || !slots_out) return GKV_ERR_INVALID;
+  const gkv::PrefixEntry* e = ctx->reg.find(key);
+  if (!e) return GKV_ERR_NOTFOUND;
+  if (e->pool != 1 || max_slots < e->n) return GKV_ERR_INVALID;
+  std::copy(e->slots.begin(), e->slots.end(), slots_out);
+  return GKV_OK;
+}
+
+int gkv_prefix_release(gkv_ctx* ctx, uint64_t key) {
+  if (!ctx) return GKV_ERR_INVALID;
+  return ctx->reg.release(key, ctx->err);
+}
+
+int gkv_prefix_evict(gkv_ctx* ctx, uint64_t key) {
+  if (!ctx) return GKV_ERR_INVALID;
+  return ctx->reg.evict(key, ctx->err);
+}
+
+int gkv_prefix_reclaim_cold(gkv_ctx* ctx, int32_t n_free_slots) {
+  if (!ctx) return GKV_ERR_INVALID;
+  return ctx->reg.reclaim_cold(n_free_slots, ctx->err);
+}
+
+int gkv_registry_stats(const gkv_ctx* ctx, gkv_registry_counts* out) {
+  if (!ctx || !out) return GKV_ERR_INVALID;
+  const gkv::RegistryCounts c = ctx->reg.counts();
+  out->resident_hot = c.resident_hot;
+  out->resident_cold = c.resident_cold;
+  out->referenced = c.referenced;
+  out->cached = c.cached;
+  out->hits = c.hits;
+  out->hot_admits = c.hot_admits;
+  out->cold_admits = c.cold_admits;
+  out->evictions = c.evictions;
   return GKV_OK;
 }
 

@@ -1096,8 +1096,12 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   auto& ring = reinterpret_cast<SM*>(smem_raw)->ring;
 
   // block -> class, KV head, split, M-tile (see ClassDesc)
+  // the last class whose first block is <= blk (block_base increases)
   int ci = 0;
-  while (ci + 1 < a.n_classes && blk >= a.classes[ci + 1].block_base) ++ci;
+  for (int hi = a.n_classes - 1; ci < hi;) {
+    const int mid = (ci + hi + 1) >> 1;
+    if (a.classes[mid].block_base <= blk) ci = mid; else hi = mid - 1;
+  }
   const ClassDesc& cl = a.classes[ci];
   const int local = blk - cl.block_base;
   const int r8 = local / kXcds;

@@ -1,6 +1,6 @@
 // Work description of one decode step, shared by the host planner and the
 // device kernels.  The whole description travels in the kernel arguments
-// (about 23 KB), so a step needs no host-to-device copy before its kernels.
+// (about 25 KB), so a step needs no host-to-device copy before its kernels.
 #pragma once
 
 #include <cstdint>
@@ -40,7 +40,7 @@ constexpr int tile_members(int group, int rb) { return kWaves * 16 * rb / group;
 
 // Limits of one step (the description must fit the kernel arguments).
 constexpr int kMaxBatch = 1024;
-constexpr int kMaxClasses = 32;
+constexpr int kMaxClasses = 64;
 
 // One distinct HOT prefix in the step ("class": every request that starts
 // with this slab).  Its prefix blocks are [block_base, block_base+n_blocks):

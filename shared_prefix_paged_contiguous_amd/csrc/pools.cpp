@@ -67,6 +67,37 @@ bool HotPool::lookup(int32_t id, int64_t* offset, int32_t* len) const {
   return true;
 }
 
+int32_t HotPool::releases_to_fit(int32_t n, const std::vector<int32_t>& ids) const {
+  const int64_t need = (static_cast<int64_t>(n) + block_ - 1) / block_;
+  std::map<int64_t, int64_t> trial = free_;
+  int64_t longest = 0;
+  for (const auto& e : trial) longest = std::max(longest, e.second);
+  for (size_t j = 0;; ++j) {
+    if (longest >= need) return static_cast<int32_t>(j);
+    if (j == ids.size()) return -1;
+    auto it = live_.find(ids[j]);
+    if (it == live_.end()) return -1;
+    int64_t off = it->second.offset;
+    int64_t len = (static_cast<int64_t>(it->second.len) + block_ - 1) / block_;
+    auto next = trial.lower_bound(off);
+    if (next != trial.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first + prev->second == off) {
+        off = prev->first;
+        len += prev->second;
+        trial.erase(prev);
+      }
+    }
+    next = trial.find(off + len);
+    if (next != trial.end()) {
+      len += next->second;
+      trial.erase(next);
+    }
+    trial.emplace(off, len);
+    longest = std::max(longest, len);
+  }
+}
+
 int64_t HotPool::free_tokens() const {
   int64_t t = 0;
   for (const auto& e : free_) t += e.second;

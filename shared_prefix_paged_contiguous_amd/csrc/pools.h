@@ -32,6 +32,10 @@ struct HotPool {
   // 0 on success; -3 when id is not live.
   int release(int32_t id);
   bool lookup(int32_t id, int64_t* offset, int32_t* len) const;
+  // Fewest slabs of `ids`, taken in that order, whose release would leave a
+  // free extent for n tokens (0 if one exists now); -1 if releasing all of
+  // them would not.  Nothing changes.
+  int32_t releases_to_fit(int32_t n, const std::vector<int32_t>& ids) const;
 
   int64_t capacity_blocks() const { return capacity_; }
   int64_t free_tokens() const;      // free blocks x block

@@ -3,7 +3,7 @@
 Given a ``workloads.Workload`` it creates a library context, replays the
 workload's placement through the context's own allocators (HOT first, COLD
 fallback for prefixes that do not fit, permuted COLD free order for the
-suffix slots), writes the prefix slabs into the HOT pool with ``hot_write``
+suffix slots) - or through its prefix registry (``registry=True``) - writes the prefix slabs into the HOT pool with ``hot_write``
 (the caller's prefill, outside the decode path), appends every suffix token
 into the COLD pool with ``cold_append``, and builds the per-request CSR slot
 table.
@@ -19,10 +19,45 @@ import torch
 from . import binding, workloads
 
 
+def prefix_key(p: int) -> int:
+    """Registry key of the workload's prefix p (any distinct 64-bit values do)."""
+    return (0x9E3779B97F4A7C15 * (p + 1)) % (1 << 64)
+
+
+def place_through_registry(w: workloads.Workload, ctx: binding.Context):
+    """Place a workload with the library's prefix registry instead of raw
+    allocations: the COLD free order is scattered as the workload's recipe
+    says, then every request takes a reference to its prefix in request order
+    (the first one admits it: HOT first, COLD when no HOT extent fits, no
+    demotion), then each request's suffix slots are popped.  Same result
+    format as ``workloads.place`` ('prefix_slots' holds the prefixes the
+    registry put in COLD)."""
+    n_p = len(w.prefix_lens)
+    out = {"prefix_id": [-1] * n_p, "prefix_offset": [-1] * n_p, "prefix_slots": {},
+           "req_slots": [None] * w.batch, "refs": {}}
+    ctx.cold_pool_alloc(w.spec.cold_capacity)
+    ctx.cold_pool_free(w.cold_perm)
+    for b in range(w.batch):
+        p = int(w.request_prefix[b])
+        if p < 0:
+            continue
+        r = ctx.prefix_acquire(prefix_key(p), w.prefix_lens[p])
+        out["refs"][p] = out["refs"].get(p, 0) + 1
+        if r["fresh"]:
+            if r["pool"] == binding.POOL_HOT:
+                out["prefix_id"][p], out["prefix_offset"][p] = r["prefix_id"], r["hot_offset"]
+            else:
+                out["prefix_slots"][p] = ctx.prefix_cold_slots(prefix_key(p), w.prefix_lens[p])
+    for b in range(w.batch):
+        out["req_slots"][b] = ctx.cold_pool_alloc(int(w.suffix_lens[b]))
+    return out
+
+
 class DecodeState:
     def __init__(self, w: workloads.Workload, device: str = "cuda", n_layers: int = 1,
                  m_sat: int = 0, force_backend: int = binding.BACKEND_AUTO,
-                 hot_capacity: Optional[int] = None, cold_capacity: Optional[int] = None):
+                 hot_capacity: Optional[int] = None, cold_capacity: Optional[int] = None,
+                 registry: bool = False):
         s = w.spec
         self.w = w
         self.device = device
@@ -40,8 +75,11 @@ class DecodeState:
             except binding.NoSpace:
                 return None
 
-        self.placement = workloads.place(w, hot_alloc, ctx.hot_pool_free, ctx.cold_pool_alloc,
-                                         ctx.cold_pool_free)
+        if registry:
+            self.placement = place_through_registry(w, ctx)
+        else:
+            self.placement = workloads.place(w, hot_alloc, ctx.hot_pool_free, ctx.cold_pool_alloc,
+                                             ctx.cold_pool_free)
         pl = self.placement
 
         n_kv, d = s.n_kv, s.head_dim

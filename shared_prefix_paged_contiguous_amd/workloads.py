@@ -194,6 +194,53 @@ def make(name_or_spec, *, seed: Optional[int] = None, dtype: Optional[str] = Non
                     q, prefix_k, prefix_v, suffix_k, suffix_v, offsets)
 
 
+def make_uniform_multi_prefix(k: int, *, prefix_len: int = 8192, batch: int = 256,
+                              suffix_range: tuple = (128, 1024), hot_capacity: int,
+                              cold_capacity: int, seed: int = 0, device: str = "cpu") -> Workload:
+    """k distinct prefixes of prefix_len tokens at the Llama-3.1-8B attention
+    shape (32q/8kv, d=128, bf16), request b on prefix b % k (batch / k
+    requests each), suffix lengths U{lo..hi}: the uniform-length multi-prefix
+    sweep of paperlayer.ai Appendix B.8 (k in {1, 4, 16, 64}, L_p = 8K,
+    B = 256).
+
+    Integer draws (numpy PCG64, seeded): suffix lengths, then the COLD free
+    order.  Values: standard normals from torch's generator on `device`
+    seeded with `seed` (Q, then each prefix's K and V, then suffix K and V),
+    rounded to bf16; drawing them on the GPU keeps multi-gigabyte prefix sets
+    off the host."""
+    import torch
+
+    spec = Spec(f"uniform_k{k}_lp{prefix_len}_b{batch}", n_q=32, n_kv=8, head_dim=128, dtype="bf16",
+                batch=batch, prefix_len=prefix_len, suffix_lo=suffix_range[0], suffix_hi=suffix_range[1],
+                hot_capacity=hot_capacity, cold_capacity=cold_capacity, n_prefixes=k,
+                prefix_len_lo=prefix_len, prefix_len_hi=prefix_len, class_lo=batch // k,
+                class_hi=batch // k, seed=seed,
+                description=f"{k} distinct prefixes of {prefix_len} tokens, B={batch} (request b on "
+                            f"prefix b % {k}), 32q/8kv, d=128, bf16, suffixes U{{{suffix_range[0]}.."
+                            f"{suffix_range[1]}}}")
+    rng = np.random.default_rng(seed)
+    suffix_lens = rng.integers(suffix_range[0], suffix_range[1] + 1, size=batch).astype(np.int64)
+    cold_perm = rng.permutation(cold_capacity).astype(np.int32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def vals(shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+    q = vals((batch, 32, 128))
+    prefix_k, prefix_v = [], []
+    for _ in range(k):
+        prefix_k.append(vals((prefix_len, 8, 128)))
+        prefix_v.append(vals((prefix_len, 8, 128)))
+    total = int(suffix_lens.sum())
+    suffix_k, suffix_v = vals((total, 8, 128)), vals((total, 8, 128))
+    offsets = np.zeros(batch + 1, dtype=np.int64)
+    np.cumsum(suffix_lens, out=offsets[1:])
+    request_prefix = (np.arange(batch) % k).astype(np.int32)
+    return Workload(spec, [prefix_len] * k, request_prefix, suffix_lens, cold_perm, [],
+                    q, prefix_k, prefix_v, suffix_k, suffix_v, offsets)
+
+
 def placement_ops(w: Workload):
     """The allocator calls that place a workload, in order.
 

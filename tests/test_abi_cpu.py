@@ -256,3 +256,13 @@ def test_workspace_bound_covers_plans():
     c = _ctx(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", hot_capacity_tokens=16384,
              cold_capacity_tokens=65536)
     assert c.workspace_size(64, 65536) > c.workspace_size(4, 100) > 0
+
+
+def test_step_rejects_more_than_64_hot_classes_before_any_device_work():
+    c = _ctx(hot_capacity_tokens=65 * BLOCK)
+    ids = [c.hot_pool_alloc(BLOCK)[0] for _ in range(65)]
+    c.bind_layer(0, 16, 16, 16, 16)   # fake aligned addresses: only host checks run below
+    c.bind_workspace(256, 1 << 24)
+    indptr = list(range(66))
+    with pytest.raises(binding.GkvError, match="more than 64 distinct HOT prefixes"):
+        c.attn_decode(0, 16, ids, indptr, 16, 16, 16, 16, batch=65, stream=0)
