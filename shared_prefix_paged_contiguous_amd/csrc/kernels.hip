@@ -518,12 +518,18 @@ __device__ __forceinline__ void load_partial_vals(const T* src, float (&v)[PER])
 // all of this wave's partial stores have completed
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One 16-byte piece of a partial row with the coherence of the agent-scope
-// stores above (sc1: written through to where every XCD reads it).  A
-// 64-bit address, so partial buffers of any size; the explicit wait in
-// wait_stores() covers it.
+// One 16-byte piece of a partial row as two agent-scope 64-bit stores
+// (written through to where every XCD reads it).  Compiler-emitted on
+// purpose: a store of more than 8 bytes reads its data registers after
+// issue, and only the compiler's hazard tracking knows to keep the next
+// instructions from overwriting them (an inline-asm 16-byte store lost the
+// last lanes' data that way).
 __device__ __forceinline__ void store_chunk(void* dst, const u32x4& v) {
-  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+  uint64_t* p = static_cast<uint64_t*>(dst);
+  const uint64_t lo = static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
+  const uint64_t hi = static_cast<uint64_t>(v[2]) | (static_cast<uint64_t>(v[3]) << 32);
+  __hip_atomic_store(p, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16 bytes of a row from 16 / sizeof(T) floats (LDS), in the dtype T
 template <typename T>
