@@ -518,6 +518,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
   a.s_o = ws + off_so;
   a.s_lse = reinterpret_cast<float*>(ws + off_sl);
+  a.narrow_ws = need < 0x7fffffffull ? 1 : 0;   // partial stores may use 32-bit offsets
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   hipEvent_t* ev = nullptr;

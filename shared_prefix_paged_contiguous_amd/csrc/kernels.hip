@@ -518,13 +518,30 @@ __device__ __forceinline__ void load_partial_vals(const T* src, float (&v)[PER])
 // all of this wave's partial stores have completed
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// One 16-byte piece of a partial row as two agent-scope 64-bit stores
-// (written through to where every XCD reads it).  Compiler-emitted on
-// purpose: a store of more than 8 bytes reads its data registers after
-// issue, and only the compiler's hazard tracking knows to keep the next
-// instructions from overwriting them (an inline-asm 16-byte store lost the
-// last lanes' data that way).
-__device__ __forceinline__ void store_chunk(void* dst, const u32x4& v) {
+// cache-policy operand of the buffer intrinsics: sc1, the bit the compiler
+// sets for agent-scope atomic stores (write through to every XCD's view)
+constexpr int kCachePolicySc1 = 16;
+
+// One 16-byte piece of a partial row, written through to where every XCD
+// reads it (sc1), by compiler-emitted stores: a store of more than 8 bytes
+// reads its data registers after issue, and only the compiler's hazard
+// tracking keeps the next instructions from overwriting them (an inline-asm
+// 16-byte store lost the last lanes' data that way).  With `narrow` (the
+// host's word that the whole workspace spans less than 2 GB) it is one
+// buffer store at a 32-bit offset from the first active lane's address,
+// which must be the lowest; otherwise two agent-scope 64-bit stores.
+__device__ __forceinline__ void store_chunk(void* dst, const u32x4& v, bool narrow) {
+  if (narrow) {
+    const uint64_t a64 = reinterpret_cast<uint64_t>(dst);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a64));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a64 >> 32));
+    const uint64_t b64 = (static_cast<uint64_t>(hi) << 32) | lo;
+    // untyped 32-bit buffer format; no bound check needed beyond 2 GB
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b64), static_cast<short>(0), 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<uint32_t>(a64 - b64), 0, kCachePolicySc1);
+    return;
+  }
   uint64_t* p = static_cast<uint64_t*>(dst);
   const uint64_t lo = static_cast<uint64_t>(v[0]) | (static_cast<uint64_t>(v[1]) << 32);
   const uint64_t hi = static_cast<uint64_t>(v[2]) | (static_cast<uint64_t>(v[3]) << 32);
@@ -1349,7 +1366,8 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
 #pragma unroll
       for (int s = 0; s < 16 / RPI; ++s)
         if (wrow0 + 16 * rb + s * RPI + rsub < rows)
-          store_chunk(static_cast<T*>(a.p_o) + static_cast<size_t>(prow_of[s]) * D + (16 / sizeof(T)) * ch, pk[s]);
+          store_chunk(static_cast<T*>(a.p_o) + static_cast<size_t>(prow_of[s]) * D + (16 / sizeof(T)) * ch, pk[s],
+                      a.narrow_ws != 0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");

@@ -97,6 +97,7 @@ struct StepArgs {
   int32_t multi_part;          // some request has more than one suffix part
   int32_t n_parts;             // suffix parts of the step
   int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
+  int32_t narrow_ws;           // the step's workspace spans less than 2 GB (32-bit store offsets)
   const void* q;
   void* out;
   float* lse;

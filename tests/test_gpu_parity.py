@@ -172,6 +172,28 @@ def test_fp32_head_dims(d):
     check(out, lse, *oracle_ref(w), **FP32_TOL)
 
 
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_largest_batch_parity(force):
+    """The largest batch one step takes (1024 requests): one shared prefix,
+    slot tables of 0..8 tokens, so many requests are prefix-only and many
+    suffix parts are one token long."""
+    s = spec(n_q=8, n_kv=2, head_dim=64, batch=1024, prefix_len=200, hot_capacity=256, suffix_lo=0,
+             suffix_hi=8, cold_capacity=16384)
+    w = workloads.make(s)
+    _, out, lse, _ = run(w, force=force)
+    check(out, lse, *oracle_ref(w))
+
+
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_most_query_heads_parity(force):
+    """The most query heads a context takes (256), 16 per KV head."""
+    s = spec(n_q=256, n_kv=16, head_dim=64, batch=3, prefix_len=100, hot_capacity=128, suffix_lo=0,
+             suffix_hi=40, cold_capacity=4096)
+    w = workloads.make(s)
+    _, out, lse, _ = run(w, force=force)
+    check(out, lse, *oracle_ref(w))
+
+
 def test_single_request_single_token():
     s = spec(batch=1, prefix_len=0, hot_capacity=0, fixed_suffix=(1,))
     w = workloads.make(s)
