@@ -286,6 +286,14 @@ def run_bench(args):
         torch.cuda.synchronize()
         ms_warm = e0.elapsed_time(e1) / args.steps
 
+    # gkv_cold_append alone: the batch's new token rows into their slots
+    e0.record(stream)
+    for i in range(args.steps):
+        ctx.cold_append(i % replicas, k_new, v_new, slots_new, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_append = e0.elapsed_time(e1) / args.steps * 1e3
+
     # per-kernel durations with HIP events recorded by the library on this stream
     ctx.kernel_timing(args.steps)
     for i in range(args.steps):
@@ -328,6 +336,7 @@ def run_bench(args):
         "step_hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": alg["step_bytes"],
         "warm_ms_per_step": round(ms_warm, 5) if ms_warm is not None else None,
+        "append_only_us": round(us_append, 2),
         "kernel_us": {k: round(v * 1e3, 2) for k, v in kern_ms.items()},
         "kernel_us_stats": kern_stats,
         "kernel_note": ("step = the step kernel of gkv_attn_decode (prefix splits, suffix parts, join); "
