@@ -322,6 +322,11 @@ typedef struct {
   int32_t joins_partials;     /* 1 if some output is joined from several partials (a HOT
                                  prefix or a multi-part slot table), inside the step kernel */
   int32_t suffix_part_tokens; /* slot-table tokens per suffix part this step */
+  int32_t folded_parts;       /* 1 if each suffix workgroup ran two parts (a short one, then a
+                                 long one): chosen for cascade steps whose parts' workgroups
+                                 overflow the workgroup slots beside the prefix while half as
+                                 many fit */
+  int32_t reserved;
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
 } gkv_plan_info;

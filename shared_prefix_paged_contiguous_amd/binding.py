@@ -57,6 +57,7 @@ class _PlanInfo(ctypes.Structure):
                 ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
                 ("joins_partials", ctypes.c_int32), ("suffix_part_tokens", ctypes.c_int32),
+                ("folded_parts", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
 
 
@@ -353,7 +354,7 @@ class Context:
     def last_plan(self) -> dict:
         p = _PlanInfo()
         self._check(self._lib.gkv_last_plan(self._h, ctypes.byref(p)), "last_plan")
-        return {f: getattr(p, f) for f, _ in _PlanInfo._fields_ if f != "pad_"}
+        return {f: getattr(p, f) for f, _ in _PlanInfo._fields_ if f not in ("pad_", "reserved")}
 
 
 def default_m_sat() -> int:

@@ -541,6 +541,8 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   ctx->last.n_suffix_parts = plan.n_parts;
   ctx->last.joins_partials = plan.multi_part;
   ctx->last.suffix_part_tokens = plan.part_tokens;
+  ctx->last.folded_parts = plan.fold;
+  ctx->last.reserved = 0;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->have_last = true;

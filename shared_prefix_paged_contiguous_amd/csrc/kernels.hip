@@ -772,11 +772,11 @@ __device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, i
 }
 
 // ------------------------------------------------------------ suffix blocks
-// One workgroup per (suffix part, KV head); see StepArgs.  Each wave runs
-// the online softmax over its quarter of the part through the slot table and
-// the four results meet in LDS.  A request without a HOT prefix whose slot
-// table is one part is finished here; otherwise the part's partial is written
-// for the request's join workgroup.
+// One (suffix part, KV head) per call; see StepArgs.  Each wave runs the
+// online softmax over its quarter of the part through the slot table and the
+// four results meet in LDS.  A request without a HOT prefix whose slot table
+// is one part is finished here; otherwise the part's partial is written for
+// the request's join workgroup.
 template <typename T, int D>
 struct SuffixSmem {
   int32_t ids[kWaves][kWaveTokens];
@@ -784,22 +784,14 @@ struct SuffixSmem {
   float lse[kWaves][16];
 };
 
-template <typename T, int D>
-__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
-  using TR = Traits<T, D>;
-  using KOp = typename TR::KOp;
-  using VVec = typename TR::VVec;
-  constexpr int PER = D / 64;
-  SuffixSmem<T, D>& sm = *reinterpret_cast<SuffixSmem<T, D>*>(smem_raw);
-  auto& lds_ids = sm.ids;
-  auto& lds_o = sm.o;
-  auto& lds_lse = sm.lse;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: so are the loop bounds
-  const int part = blk / a.n_kv;
-  const int gk = blk - part * a.n_kv;
-  if (part >= a.n_parts) return;   // grid padding
+// A wave's piece of one suffix part: the part's request, its slot-table
+// range [tb0, tb1), and the wave's quarter [w0, w0 + len) of the part
+// (quarters are whole 32-token tiles, `piece` tokens long but the last).
+struct SuffixPiece {
+  int b, w0, len, tb1, piece;
+  bool single;   // the request's slot table is this one part
+};
+__device__ __forceinline__ SuffixPiece suffix_piece(const StepArgs& a, int part, int wave) {
   // rank: the last r with ranks[r].part0 <= part, which is the part itself
   // when every request has one part
   int lo = part;
@@ -812,14 +804,98 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     }
   }
   const RankDesc rd = a.ranks[lo];
-  const int b = rd.req;
   const int j = part - rd.part0;
-  const bool single = parts_of(rd) == 1;
   const int tb0 = rd.tok0, tb1 = rd.tok1;
   const int p0 = min(tb1, tb0 + j * kSuffixPart), p1 = min(tb1, p0 + kSuffixPart);
-  const int piece = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
-  const int w0 = min(p1, p0 + wave * piece), w1 = min(p1, w0 + piece);
-  const int len = w1 - w0;
+  SuffixPiece pc;
+  pc.b = rd.req;
+  pc.tb1 = tb1;
+  pc.single = parts_of(rd) == 1;
+  pc.piece = (((p1 - p0 + kWaves - 1) / kWaves) + kSuffixTile - 1) / kSuffixTile * kSuffixTile;
+  pc.w0 = min(p1, p0 + wave * pc.piece);
+  pc.len = min(p1, pc.w0 + pc.piece) - pc.w0;
+  return pc;
+}
+
+// The four wave results of one part meet in LDS (slot w = wave w's piece):
+// wave w joins columns w, w+4, ... and writes the request's output (a
+// request without a HOT prefix whose slot table is this one part) or the
+// part's partial.  Returns true for the former.
+template <typename T, int D>
+__device__ __forceinline__ bool suffix_publish(const StepArgs& a, SuffixSmem<T, D>& sm, int part, int b,
+                                               bool single, int gk, int wave, int lane) {
+  constexpr int PER = D / 64;
+  const int G = a.group;
+  const bool final_here = single && table_at(a.req_class, b) < 0;
+  for (int col = wave; col < G; col += kWaves) {
+    const int hc = gk * G + col;
+    float acc[PER];
+    const float l2 = join_parts<PER, 4>(
+        kWaves, lane, [&](int p) { return sm.lse[p][col]; },
+        [&](int p, float (&v)[PER]) {
+#pragma unroll
+          for (int j = 0; j < PER; ++j) v[j] = sm.o[p][col][PER * lane + j];
+        },
+        acc);
+    if (final_here) {
+      T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + hc) * D + PER * lane;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
+      if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
+    } else {
+      const size_t row = static_cast<size_t>(part) * a.n_q + hc;
+      store_partial_vals<T, PER>(static_cast<T*>(a.s_o) + row * D + PER * lane, acc);
+      if (lane == 0) store_partial(a.s_lse + row, l2);
+    }
+  }
+  return final_here;
+}
+
+// A wave's result for one part into its LDS slot (column n, lane group g).
+template <typename T, int D>
+__device__ __forceinline__ void suffix_to_lds(SuffixSmem<T, D>& sm, int wave, int n, int g, bool col_ok,
+                                              const float (&o)[D / 4], float lse2) {
+  if (col_ok) {
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k)
+      *reinterpret_cast<f32x4*>(&sm.o[wave][n][(D / 4) * g + 4 * k]) =
+          f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+    if (g == 0) sm.lse[wave][n] = lse2;
+  }
+}
+
+// Fused decode step: copies KV head gk's share of request b's new token
+// (k_new/v_new row) into its COLD slot; slots outside the pool are skipped.
+// The eight KV-head workgroups of the part write the whole row; nothing else
+// reads that slot in the step.
+template <typename T, int D>
+__device__ __forceinline__ void suffix_copy_new(const StepArgs& a, int b, int gk, int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
+  static_assert(CH <= 32, "a row copy takes at most half a wave");
+  const int slot = a.new_slots[b];
+  if (slot >= 0 && slot < a.cold_cap) {
+    const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
+    const size_t dst = (static_cast<size_t>(slot) * a.n_kv + gk) * D;
+    const int ch = lane & 31;
+    const T* src = static_cast<const T*>(lane < 32 ? a.k_new : a.v_new) + new_row;
+    T* to = static_cast<T*>(const_cast<void*>(lane < 32 ? a.k_cold : a.v_cold)) + dst;
+    if (ch < CH) reinterpret_cast<u32x4*>(to)[ch] = reinterpret_cast<const u32x4*>(src)[ch];
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk, uint8_t* smem_raw) {
+  using TR = Traits<T, D>;
+  using KOp = typename TR::KOp;
+  using VVec = typename TR::VVec;
+  SuffixSmem<T, D>& sm = *reinterpret_cast<SuffixSmem<T, D>*>(smem_raw);
+  auto& lds_ids = sm.ids;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: so are the loop bounds
+  const SuffixPiece pc = suffix_piece(a, part, wave);
+  const int b = pc.b, w0 = pc.w0, len = pc.len, tb1 = pc.tb1;
+  const bool single = pc.single;
 
   const int n = lane & 15, g = lane >> 4;
   const int G = a.group;
@@ -839,26 +915,12 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
     const int cap1 = a.cold_cap - 1;
     // Fused decode step: the wave whose piece ends the slot table reads the
     // table's last token (the request's new one) from k_new/v_new, and
-    // copies this KV head's share of it into the new slot (the eight KV-head
-    // workgroups of the part write the whole row; nothing else reads that
-    // slot in the step).  Slots outside the pool are skipped.
-    const bool fresh = a.k_new != nullptr && w1 == tb1;
+    // copies this KV head's share of it into the new slot.
+    const bool fresh = a.k_new != nullptr && w0 + len == tb1;
     const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
     const T* knew = static_cast<const T*>(a.k_new) + new_row;
     const T* vnew = static_cast<const T*>(a.v_new) + new_row + TR::EPB * n;
-    if (fresh) {
-      constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
-      static_assert(CH <= 32, "a row copy takes at most half a wave");
-      const int slot = a.new_slots[b];
-      if (slot >= 0 && slot < a.cold_cap) {
-        const size_t dst = (static_cast<size_t>(slot) * a.n_kv + gk) * D;
-        const int ch = lane & 31;
-        const T* src = static_cast<const T*>(lane < 32 ? a.k_new : a.v_new) + new_row;
-        T* to = static_cast<T*>(const_cast<void*>(lane < 32 ? a.k_cold : a.v_cold)) + dst;
-        if (ch < CH)
-          reinterpret_cast<u32x4*>(to)[ch] = reinterpret_cast<const u32x4*>(src)[ch];
-      }
-    }
+    if (fresh) suffix_copy_new<T, D>(a, b, gk, lane);
 
     // the piece's slot ids, clamped into the pool, staged in this wave's
     // LDS row once: no tile waits on a slot-id load.  The loads of 256 ids
@@ -951,44 +1013,30 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   }
 
   // the wave pieces meet in LDS
-  if (col_ok) {
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k)
-      *reinterpret_cast<f32x4*>(&lds_o[wave][n][(D / 4) * g + 4 * k]) =
-          f32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-    if (g == 0) lds_lse[wave][n] = lse2;
-  }
+  suffix_to_lds<T, D>(sm, wave, n, g, col_ok, o, lse2);
   __syncthreads();
-
-  // epilogue: wave w joins columns w, w+4, ... over the four pieces
-  const bool final_here = single && table_at(a.req_class, b) < 0;
-  for (int col = wave; col < G; col += kWaves) {
-    const int hc = gk * G + col;
-    float acc[PER];
-    const float l2 = join_parts<PER, 4>(
-        kWaves, lane, [&](int p) { return lds_lse[p][col]; },
-        [&](int p, float (&v)[PER]) {
-#pragma unroll
-          for (int j = 0; j < PER; ++j) v[j] = lds_o[p][col][PER * lane + j];
-        },
-        acc);
-    if (final_here) {
-      T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + hc) * D + PER * lane;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) dst[k] = static_cast<T>(acc[k]);
-      if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
-    } else {
-      const size_t row = static_cast<size_t>(part) * a.n_q + hc;
-      store_partial_vals<T, PER>(static_cast<T*>(a.s_o) + row * D + PER * lane, acc);
-      if (lane == 0) store_partial(a.s_lse + row, l2);
-    }
-  }
-  if (final_here) return;
+  if (suffix_publish<T, D>(a, sm, part, b, single, gk, wave, lane)) return;
 
   // this part's partial is written: count it for the request's join
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) arrive(a, b, gk);
+}
+
+// Suffix block i: part q = i / n_kv for KV head i % n_kv, or, folded, part
+// n_parts-1-q (the shorter) and then part q; the barrier between the two
+// frees the LDS.  Folded, blocks q >= ceil(n_parts / 2) are grid padding.
+template <typename T, int D>
+__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
+  const int q = blk / a.n_kv;
+  const int gk = blk - q * a.n_kv;
+  if (q >= (a.fold ? (a.n_parts + 1) / 2 : a.n_parts)) return;   // grid padding
+  const int first = a.fold ? a.n_parts - 1 - q : q;
+  if (first > q) {
+    suffix_part<T, D>(a, first, gk, smem_raw);
+    __syncthreads();
+  }
+  suffix_part<T, D>(a, q, gk, smem_raw);
 }
 
 // ------------------------------------------------------------ prefix kernel

@@ -181,7 +181,17 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   }
   a.n_parts = static_cast<int32_t>(parts);
   a.tail = kArgsTail;
-  a.suffix_blocks = static_cast<int32_t>(round_up(parts * n_kv, kGroup));
+  // fold pairs of parts when the parts' workgroups overflow the slots the
+  // prefix leaves and the folded ones fit (cascade steps only: dense fills
+  // every slot with prefix work).  Folding into a second round of paired
+  // workgroups is slower than not folding.
+  const int64_t free_slots = kStepSlots - static_cast<int64_t>(a.prefix_blocks);
+  const bool fold = backend == GKV_BACKEND_CASCADE && parts > 1 && parts * n_kv > free_slots &&
+                    ceil_div(parts, 2) * n_kv <= free_slots;
+  a.fold = fold ? 1 : 0;
+  a.pad1_ = 0;
+  a.suffix_blocks = static_cast<int32_t>(round_up((fold ? ceil_div(parts, 2) : parts) * n_kv, kGroup));
+  plan.fold = a.fold;
   a.multi_part = multi;
   a.need_merge = multi || n_classes > 0;
   a.join_blocks = a.need_merge ? batch * n_kv : 0;

@@ -35,6 +35,7 @@ struct Plan {
   int64_t suffix_rows = 0;      // suffix partial rows
   int32_t part_tokens = 0;      // slot-table tokens per suffix part
   int32_t rb = 1;               // row blocks per wave of the prefix tiles
+  int32_t fold = 0;             // suffix workgroups run folded pairs of parts
 };
 
 // Rule alone: dense iff batch * group >= m_sat (unless forced).

@@ -33,6 +33,7 @@ constexpr int kMaxSplits = 64;    // L splits per prefix class
 constexpr int kHotBlock = 32;     // tokens per HOT block; slabs start on block boundaries
 constexpr int kRingBytes = 64 * 1024;   // LDS ring of a prefix workgroup (K+V images of 3..8 blocks)
 constexpr int kXcds = 8;          // MI355X: workgroups go to the 8 XCDs round-robin
+constexpr int kStepSlots = 512;   // MI355X: 256 CUs x 2 resident step workgroups
 
 // Requests per prefix M-tile: a tile holds whole requests (all G query
 // heads of a member for the tile's KV head), at most 64 * RB rows.
@@ -73,6 +74,15 @@ struct ClassDesc {
 // KV head), placed after all prefix and suffix work in the grid, waits for
 // the count and joins the partials into the output.
 //
+// Folding (cascade steps): when the parts' workgroups would not all fit in
+// the workgroup slots the prefix leaves but half as many would, suffix block
+// i runs two parts for its KV head, the short part n_parts-1-q first and then
+// the long part q (q = i / n_kv).  Ranked longest first, the pairs carry
+// about equal work, so all suffix work is resident from the start instead of
+// a second round of short workgroups, each bound by its fixed round trips,
+// running after the prefix ends; and each workgroup finishes on a long part,
+// which keeps many loads in flight to the end.
+//
 // Grid: prefix blocks, then suffix blocks, then batch * n_kv join blocks.
 // Prefix and suffix blocks never wait, and every join block follows all of
 // them in each XCD's (in-order) dispatch, so the joins' waits end.
@@ -98,6 +108,8 @@ struct StepArgs {
   int32_t n_parts;             // suffix parts of the step
   int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
   int32_t narrow_ws;           // the step's workspace spans less than 2 GB (32-bit store offsets)
+  int32_t fold;                // suffix block i runs parts n_parts-1-i/n_kv and i/n_kv (see above)
+  int32_t pad1_;
   const void* q;
   void* out;
   float* lse;

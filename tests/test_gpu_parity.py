@@ -358,6 +358,56 @@ def test_long_suffixes_span_several_parts(force):
     check(out, lse, *oracle_ref(w))
 
 
+def _fold_lengths(batch):
+    # short tables, one prefix-only request and one two-part table
+    lens = np.random.default_rng(batch).integers(1, 200, batch)
+    lens[3], lens[7] = 0, 5000
+    return tuple(int(x) for x in lens)
+
+
+@pytest.mark.parametrize("batch,dtype", [(64, "bf16"), (65, "bf16"), (65, "f32")])
+def test_folded_suffix_parts_parity(batch, dtype):
+    """When the suffix parts' workgroups overflow the slots the prefix leaves
+    and half as many fit, each suffix workgroup runs two parts (short, then
+    long).  An odd part count leaves the middle part alone; a two-part table
+    and a prefix-only request ride along."""
+    s = spec(n_q=32, n_kv=8, head_dim=64, dtype=dtype, batch=batch, prefix_len=256, hot_capacity=256,
+             cold_capacity=24000, fixed_suffix=_fold_lengths(batch))
+    w = workloads.make(s)
+    st, out, lse, backend = run(w, force=CASCADE)
+    plan = st.ctx.last_plan()
+    assert plan["folded_parts"] == 1 and plan["n_suffix_parts"] == batch + 1
+    assert plan["n_suffix_blocks"] == -(-(-(-(batch + 1) // 2) * 8) // 32) * 32
+    tol = FP32_TOL if dtype == "f32" else {}
+    ref = oracle_ref(w)
+    check(out, lse, *ref, **tol)
+    # repeated calls: each part is counted once per call (padding workgroups
+    # of the folded grid do nothing), so the join counters start at zero
+    for _ in range(3):
+        out, lse = st.new_outputs()
+        st.run(out, lse)
+        torch.cuda.synchronize()
+        check(out, lse, *ref, **tol)
+
+
+def test_fold_rule():
+    """No folding when the parts fit beside the prefix, when even half as
+    many would not, for suffix-only steps whose parts fill the slots exactly,
+    or under the dense backend."""
+    few = workloads.make(spec(n_kv=8, batch=40, prefix_len=256, hot_capacity=256, fixed_suffix=(9,) * 40))
+    st, *_ = run(few, force=CASCADE)
+    assert st.ctx.last_plan()["folded_parts"] == 0
+    only = workloads.make(spec(n_kv=8, batch=64, prefix_len=0, hot_capacity=0, fixed_suffix=(9,) * 64))
+    st, *_ = run(only, force=CASCADE)
+    assert st.ctx.last_plan()["folded_parts"] == 0 and st.ctx.last_plan()["n_suffix_blocks"] == 512
+    many = workloads.make(spec(n_q=32, n_kv=8, head_dim=64, batch=128, prefix_len=256, hot_capacity=256,
+                               cold_capacity=4096, fixed_suffix=(9,) * 128))
+    for force in (CASCADE, DENSE):              # 1024 part workgroups, 480 free slots
+        st, out, lse, _ = run(many, force=force)
+        assert st.ctx.last_plan()["folded_parts"] == 0
+        check(out, lse, *oracle_ref(many))
+
+
 # ------------------------------------------------------- fused decode step
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
@@ -374,6 +424,9 @@ def _fused_cases():
         "fallback_to_cold": (spec(batch=4, prefix_len=900, fixed_suffix=(3, 50, 129, 400)), AUTO, "cold"),
         "multi_part": (spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
                             fixed_suffix=(5000, 10, 1, 9000)), AUTO, None),
+        "folded": (spec(n_q=32, n_kv=8, head_dim=64, batch=65, prefix_len=256, hot_capacity=256,
+                        cold_capacity=24000, fixed_suffix=tuple(max(1, n) for n in _fold_lengths(65))),
+                   CASCADE, None),
     }
 
 
@@ -408,6 +461,7 @@ def test_fused_step_equals_append_then_attend(case):
     bb = sb.step(out_b, lse_b, k_new, v_new, slots)
     torch.cuda.synchronize()
     assert ba == bb
+    assert sb.ctx.last_plan()["folded_parts"] == (case == "folded")
     assert torch.equal(_bits(out_a), _bits(out_b))
     assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
     for i in (2, 3):                                  # k_cold, v_cold
