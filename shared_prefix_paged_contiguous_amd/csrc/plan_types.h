@@ -1,6 +1,6 @@
 // Work description of one decode step, shared by the host planner and the
 // device kernels.  The whole description travels in the kernel arguments
-// (about 25 KB), so a step needs no host-to-device copy before its kernels.
+// (about 24 KB), so a step needs no host-to-device copy before its kernels.
 #pragma once
 
 #include <cstdint>
