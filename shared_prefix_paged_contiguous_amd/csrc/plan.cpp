@@ -133,26 +133,46 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   int64_t units = 0;
   for (int32_t c = 0; c < n_classes; ++c)
     units += static_cast<int64_t>(n_kv) * ceil_div(class_size[c], tm) * a.classes[c].len;
-  const int64_t split_tokens = std::max<int64_t>(
+  // one split length for every class; returns the prefix blocks it makes
+  auto split_classes = [&](int64_t split_tokens) {
+    int32_t nb = 0;
+    for (int32_t c = 0; c < n_classes; ++c) {
+      ClassDesc& cd = a.classes[c];
+      const int64_t len = cd.len;
+      int64_t s = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, ceil_div(len, split_tokens)));
+      const int64_t chunk = round_up(ceil_div(len, s), kPrefixTile);
+      s = ceil_div(len, chunk);
+      cd.n_splits = static_cast<int32_t>(s);
+      cd.chunk = static_cast<int32_t>(chunk);
+      cd.m_tiles = static_cast<int32_t>(ceil_div(cd.n_members, tm));
+      cd.n_groups = n_kv * cd.n_splits;
+      cd.block_base = nb;
+      cd.n_blocks = kXcds * static_cast<int32_t>(ceil_div(cd.n_groups, kXcds)) * cd.m_tiles;
+      cd.pad_ = 0;
+      nb += cd.n_blocks;
+    }
+    return static_cast<int32_t>(round_up(nb, kGroup));
+  };
+  const int64_t split0 = std::max<int64_t>(
       kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), target), kPrefixTile));
-  int32_t max_splits = 0;
-  int32_t blocks = 0;
-  for (int32_t c = 0; c < n_classes; ++c) {
-    ClassDesc& cd = a.classes[c];
-    const int64_t len = cd.len;
-    int64_t s = std::min<int64_t>(kMaxSplits, std::max<int64_t>(1, ceil_div(len, split_tokens)));
-    const int64_t chunk = round_up(ceil_div(len, s), kPrefixTile);
-    s = ceil_div(len, chunk);
-    cd.n_splits = static_cast<int32_t>(s);
-    cd.chunk = static_cast<int32_t>(chunk);
-    cd.m_tiles = static_cast<int32_t>(ceil_div(cd.n_members, tm));
-    cd.n_groups = n_kv * cd.n_splits;
-    cd.block_base = blocks;
-    cd.n_blocks = kXcds * static_cast<int32_t>(ceil_div(cd.n_groups, kXcds)) * cd.m_tiles;
-    cd.pad_ = 0;
-    blocks += cd.n_blocks;
-    max_splits = std::max(max_splits, cd.n_splits);
+  int32_t blocks = split_classes(split0);
+  // Cascade: when folded suffix pairs (see below) would not fit beside this
+  // prefix grid but would beside a somewhat smaller one, lengthen the splits
+  // (up to twice) until they fit.
+  if (backend == GKV_BACKEND_CASCADE && n_classes > 0) {
+    int64_t parts = 0;
+    for (int32_t b = 0; b < batch; ++b)
+      parts += std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
+    const int64_t pairs = ceil_div(parts, 2) * n_kv;
+    if (parts > 1 && parts * n_kv > kStepSlots - blocks && pairs > kStepSlots - blocks &&
+        pairs <= kStepSlots - kGroup) {
+      int64_t st = split0 + kPrefixTile;
+      while (st <= 2 * split0 && split_classes(st) > kStepSlots - pairs) st += kPrefixTile;
+      blocks = split_classes(st <= 2 * split0 ? st : split0);   // the classes keep the last call's splits
+    }
   }
+  int32_t max_splits = 0;
+  for (int32_t c = 0; c < n_classes; ++c) max_splits = std::max(max_splits, a.classes[c].n_splits);
   a.prefix_blocks = static_cast<int32_t>(round_up(blocks, kGroup));
   a.max_splits = max_splits;
   plan.prefix_blocks = a.prefix_blocks;

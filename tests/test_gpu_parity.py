@@ -408,6 +408,20 @@ def test_fold_rule():
         check(out, lse, *oracle_ref(many))
 
 
+def test_prefix_splits_lengthen_so_pairs_fit():
+    """Qwen-2.5-14B TP=2 slice (128 requests, 4 KV heads, a 16K prefix): the
+    first split length makes 288 prefix workgroups, beside which the 256
+    folded suffix workgroups would not fit; the splits are lengthened until
+    they do (256 prefix workgroups).  Sampled requests match the oracle."""
+    w = workloads.make("qwen14b_tp2_lp16k_b128")
+    st, out, lse, backend = run(w, force=CASCADE)
+    plan = st.ctx.last_plan()
+    assert plan["folded_parts"] == 1 and plan["n_suffix_blocks"] == 256
+    assert plan["n_prefix_blocks"] == 256
+    req = [0, 1, 63, 127]
+    check(out, lse, *oracle_ref(w, requests=req), requests=req)
+
+
 # ------------------------------------------------------- fused decode step
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
