@@ -784,8 +784,8 @@ struct SuffixSmem {
   float lse[kWaves][16];
 };
 
-// A wave's piece of one suffix part: the part's request, its slot-table
-// range [tb0, tb1), and the wave's quarter [w0, w0 + len) of the part
+// A wave's piece of one suffix part: the part's request b, the end tb1 of
+// its slot-table range, and the wave's quarter [w0, w0 + len) of the part
 // (quarters are whole 32-token tiles, `piece` tokens long but the last).
 struct SuffixPiece {
   int b, w0, len, tb1, piece;
