@@ -45,11 +45,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(w, st):
+def algorithmic(w, st, fused=True):
     """Bytes and flops the method must move / do in one step, whole step and
     per kernel.  K/V of each distinct HOT prefix count once (read once per
-    step), every suffix token once; partials and work lists are overhead and
-    do not count."""
+    step), every suffix token once (the current token included), the slot
+    ids, the row pointers, q, out and lse once; partials and work lists are
+    overhead and do not count.  The append writes each new token's K/V row and
+    reads its slot id.  Fused (gkv_decode_step), the new token's K/V are read
+    once, from the caller's rows, as part of the suffix; as two launches
+    (gkv_cold_append, then gkv_attn_decode) the append also reads them and the
+    attention reads them again from the pool, which is real traffic of that
+    path."""
     s = w.spec
     e = 2 if s.dtype == "bf16" else 4
     d, n_kv, n_q, bsz = s.head_dim, s.n_kv, s.n_q, w.batch
@@ -58,20 +64,23 @@ def algorithmic(w, st):
     pre_tokens = sum(st.ctx.hot_prefix_info(c)[1] for c in classes)
     tab = np.diff(st.indptr_h.astype(np.int64))
     suf_tokens = int(tab.sum())
-    n_pre_req, n_suf_req = int((ids >= 0).sum()), int((tab > 0).sum())
+    n_new = int((tab > 0).sum())
     q_row = n_q * d * e
     kv_row = n_kv * d * e
-    # the step kernel streams every prefix and suffix K/V byte, the slot ids
-    # and q, and writes out and lse (partials are overhead)
-    k = {"step": 2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + bsz * q_row
-         + bsz * q_row + 4 * bsz * n_q}
-    append = 2 * 2 * n_suf_req * kv_row + 4 * n_suf_req
-    step = (2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + 4 * (bsz + 1)
-            + bsz * q_row + bsz * q_row + 4 * bsz * n_q + append)
+    attend = (2 * pre_tokens * kv_row + 2 * suf_tokens * kv_row + 4 * suf_tokens + 4 * (bsz + 1)
+              + bsz * q_row + bsz * q_row + 4 * bsz * n_q)
+    append_write = 2 * n_new * kv_row + 4 * n_new
+    append_read = 2 * n_new * kv_row
+    if fused:
+        k = {"step": attend + append_write}
+        step = attend + append_write
+    else:
+        k = {"step": attend}
+        step = attend + append_write + append_read
     group = n_q // n_kv
     flops_prefix = sum(4 * int((ids == c).sum()) * group * st.ctx.hot_prefix_info(c)[1] * d * n_kv
                        for c in classes)
-    return {"kernel_bytes": k, "append_bytes": append, "step_bytes": step,
+    return {"kernel_bytes": k, "append_bytes": append_write + append_read, "step_bytes": step,
             "prefix_flops": flops_prefix, "suffix_flops": 4 * n_q * d * suf_tokens,
             "prefix_tokens": pre_tokens, "suffix_tokens": suf_tokens}
 
@@ -166,22 +175,25 @@ def cpu_baseline(w, target_s: float):
                       f"threads={threads}, host cpus={os.cpu_count()}; {t_used:.1f} s of oracle time"}
 
 
-def build_state(w, replicas, force):
+def build_state(w, replicas, force, partials="input"):
     from shared_prefix_paged_contiguous_amd.harness import DecodeState
-    return DecodeState(w, n_layers=replicas, force_backend=force)
+    return DecodeState(w, n_layers=replicas, force_backend=force, partial_dtype=partials)
 
 
 def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
-    """Measured streaming ceilings of this GPU, a second denominator beside the
-    8 TB/s data-sheet peak: the best plain read of n_bytes among a row sum and
-    a matrix-vector product over a [n/8192, 4096] bf16 matrix (both read every
-    byte once; a flat tensor sum reads slower here), and a plain device copy
-    (n_bytes read + n_bytes written); best of `reps` each."""
+    """Measured read ceiling of this GPU, a second denominator beside the
+    8 TB/s data-sheet peak: the library's plain streaming-read kernel
+    (gkv_stream_read: consecutive lanes read consecutive 16-byte vectors,
+    eight loads in flight per lane) over a 1 GiB buffer, at several grid
+    sizes, best of `reps` each; and, for context, a device copy (torch)."""
     import torch
+
+    from shared_prefix_paged_contiguous_amd import binding
+
     x = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
-    m = x.view(-1, 4096)
-    vec = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def best(fn):
@@ -189,21 +201,24 @@ def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
         torch.cuda.synchronize()
         t = []
         for _ in range(reps):
-            e0.record()
+            e0.record(stream)
             fn()
-            e1.record()
+            e1.record(stream)
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1) * 1e-3)
         return min(t)
 
-    reads = {"row_sum": n_bytes / best(lambda: m.sum(dim=1)) / 1e9,
-             "gemv": n_bytes / best(lambda: torch.mv(m, vec)) / 1e9}
+    reads = {}
+    for wg in (512, 1024, 2048, 4096, 8192):
+        reads[wg] = n_bytes / best(lambda: binding.stream_read(x, n_bytes, wg, sink, stream)) / 1e9
     copy = 2 * n_bytes / best(lambda: y.copy_(x)) / 1e9
-    del x, y, m
+    del x, y
     torch.cuda.empty_cache()
-    how = max(reads, key=reads.get)
-    return {"read_gbps": round(reads[how], 1), "read_kernel": how, "copy_gbps": round(copy, 1),
-            "bytes": n_bytes, "how": "best of %d per kernel over a 1 GiB bf16 buffer" % reps}
+    wg = max(reads, key=reads.get)
+    return {"read_gbps": round(reads[wg], 1), "read_kernel": f"gkv_stream_read, {wg} workgroups",
+            "read_gbps_by_workgroups": {str(k): round(v, 1) for k, v in reads.items()},
+            "copy_gbps": round(copy, 1), "bytes": n_bytes,
+            "how": "best of %d per grid size over a 1 GiB buffer; copy = torch copy_ (read + write)" % reps}
 
 
 def step_inputs(w, st):
@@ -232,8 +247,8 @@ def run_bench(args):
     force = {"auto": binding.BACKEND_AUTO, "cascade": binding.BACKEND_CASCADE,
              "dense": binding.BACKEND_DENSE}[args.backend]
     replicas = args.replicas or max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
-    st = build_state(w, replicas, force)
-    alg = algorithmic(w, st)
+    st = build_state(w, replicas, force, args.partials)
+    alg = algorithmic(w, st, fused=not args.separate)
     k_new, v_new, slots_new = step_inputs(w, st)
     out, lse = st.new_outputs()
     ctx = st.ctx
@@ -273,8 +288,8 @@ def run_bench(args):
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
     plan = ctx.last_plan()
-    log(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step (wall {wall*1e3/args.steps:.1f} us/step), "
-        f"backend={binding.BACKEND_NAMES[backend]}, host plan {plan['host_plan_us']:.2f} us")
+    log(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step (host wall {wall*1e6/args.steps:.1f} us/step), "
+        f"backend={binding.BACKEND_NAMES[backend]}")
 
     # same-layer ("warm", cache-resident) timing, reported for contrast only
     ms_warm = None
@@ -300,6 +315,22 @@ def run_bench(args):
         step(i)
     per = ctx.kernel_timing_read(args.steps)
     ctx.kernel_timing(0)
+
+    # host cost of a step inside the library (validation, planning, launch),
+    # read after each call: the pages' dispatch-overhead claim is about this
+    plan_us, call_us = [], []
+    for i in range(args.steps):
+        step(i)
+        p = ctx.last_plan()
+        plan_us.append(p["host_plan_us"])
+        call_us.append(p["host_call_us"])
+    torch.cuda.synchronize()
+    host = {"plan_us_median": round(float(np.median(plan_us)), 3),
+            "call_us_median": round(float(np.median(call_us)), 3),
+            "call_us_p90": round(float(np.percentile(call_us, 90)), 3),
+            "calls": len(call_us),
+            "what": "gkv_decode_step inside the library: validation + class grouping + backend rule + "
+                    "work split (plan) and the kernel launch (call), steady clock"}
     kern_ms = {"step": float(per.mean())}
     kern_stats = {"mean": round(float(per.mean()) * 1e3, 2), "median": round(float(np.median(per)) * 1e3, 2),
                   "min": round(float(per.min()) * 1e3, 2), "max": round(float(per.max()) * 1e3, 2),
@@ -307,7 +338,7 @@ def run_bench(args):
     log(f"[bench] kernel avg us: " + ", ".join(f"{k}={v*1e3:.1f}" for k, v in kern_ms.items()))
 
     dom = max(kern_ms, key=kern_ms.get)
-    dom_bytes = alg["kernel_bytes"][dom] + (0 if args.separate else alg["append_bytes"])
+    dom_bytes = alg["kernel_bytes"][dom]
     achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": counter_traffic(s.name),
@@ -344,7 +375,11 @@ def run_bench(args):
                         "step = the one launch of gkv_decode_step: new tokens appended, prefix splits, "
                         "suffix parts and their join"),
         "step_launches": 2 if args.separate else 1,
-        "host_plan_us": round(plan["host_plan_us"], 3),
+        "partials": st.ctx.partial_dtype,
+        "host_plan_us": host["plan_us_median"],
+        "host_call_us": host["call_us_median"],
+        "host_call_frac_of_step": round(host["call_us_median"] / (ms_step * 1e3), 5),
+        "host": host,
         "roofline": roofline,
         "stream_ceiling": ceiling,
     }
@@ -584,6 +619,9 @@ def main():
     ap.add_argument("--workload", default="llama8b_lp16k_b64")
     ap.add_argument("--backend", default="auto", choices=["auto", "cascade", "dense"])
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--partials", default="input", choices=["input", "f32"],
+                    help="element type of the step's partial results (workspace) before their join: "
+                         "the input dtype (library default) or fp32")
     ap.add_argument("--separate", action="store_true",
                     help="time gkv_cold_append + gkv_attn_decode (two launches) instead of gkv_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -35,6 +35,10 @@
  *     call coordinate through counters kept in it.
  *   - Element types: GKV_F32 (float) or GKV_BF16 (bfloat16, round to nearest
  *     even on output).  All arithmetic accumulates in fp32.
+ *   - Device: the kernels are built for gfx950 (CDNA4) only.  The first
+ *     device call of a context reads the current device's compute units
+ *     (and from them its XCDs, 32 compute units each) and refuses any other
+ *     architecture with GKV_ERR_DEVICE; a context then stays on that device.
  */
 #ifndef GKV_H
 #define GKV_H
@@ -56,6 +60,13 @@ typedef enum {
 
 enum { GKV_F32 = 0, GKV_BF16 = 1 };
 
+/* Element type of the partial results a step keeps in its workspace (prefix
+ * splits, suffix parts) before their log-sum-exp join. */
+enum {
+  GKV_PARTIALS_INPUT = 0,   /* the input dtype (bf16 inputs: bf16 partials) */
+  GKV_PARTIALS_F32 = 1      /* fp32 */
+};
+
 enum {
   GKV_BACKEND_AUTO = 0,     /* per step: dense iff M_eff >= m_sat */
   GKV_BACKEND_CASCADE = 1,  /* split-K prefix kernel reading each slab once */
@@ -72,6 +83,7 @@ typedef struct {
   int64_t cold_capacity_tokens;  /* C_cold >= 0, < 2^31 */
   int32_t m_sat;                 /* dense threshold on M_eff; <= 0 = library default */
   int32_t force_backend;         /* GKV_BACKEND_*; AUTO for the per-step rule */
+  int32_t partials;              /* GKV_PARTIALS_INPUT (default) or GKV_PARTIALS_F32 */
 } gkv_config;
 
 typedef struct {
@@ -329,8 +341,36 @@ typedef struct {
   int32_t reserved;
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
+  double host_call_us;        /* host time of the whole call: validation, planning and the
+                                 kernel launch (the call returns right after the launch) */
 } gkv_plan_info;
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
+
+/* Status of the steps run on the bound workspace since it was bound or last
+ * read: *joins_timed_out = the number of (request, KV head) joins that gave
+ * up waiting for their partial results at the spin limit (their outputs are
+ * not valid).  The join of a step's partials runs inside the step kernel and
+ * waits for the partials' arrival counts with a bounded wait, so that the
+ * kernel always ends; a well-formed step never reaches the bound.  Enqueues
+ * a 4-byte copy on `stream` and synchronises it.  After a nonzero status the
+ * next step first clears the workspace's counters and status word.
+ * GKV_ERR_INVALID without a bound workspace. */
+int gkv_step_status(gkv_ctx* ctx, void* stream, int32_t* joins_timed_out);
+
+/* Bound of the join's wait, in polls (each an agent-scope load and a short
+ * sleep; default 65536, about 0.1 s): polls >= 0 sets it, -1 restores the
+ * default.  For tests of the give-up path (e.g. 0: a join that finds its
+ * partials missing gives up at once, and the kernel still ends normally). */
+int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls);
+
+/* Measurement: a plain streaming read of `bytes` (a multiple of 16) at dev
+ * (16-byte aligned) by `workgroups` workgroups of 256 lanes, each lane keeping
+ * eight 16-byte loads in flight; the data is discarded (sink_dev: 4 bytes of
+ * device memory that the kernel practically never writes).  Timed by the
+ * caller on `stream`, it gives the device's achievable read bandwidth, the
+ * ceiling the attention kernels are compared with beside the data-sheet
+ * peak.  Needs no context.  Asynchronous. */
+int gkv_stream_read(const void* dev, size_t bytes, int32_t workgroups, uint32_t* sink_dev, void* stream);
 
 /* Kernel timing, for measurement.  With capacity > 0, each following
  * gkv_attn_decode launches its step kernel (prefix splits, suffix parts and

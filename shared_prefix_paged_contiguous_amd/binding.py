@@ -22,6 +22,7 @@ GKV_OK, GKV_ERR_INVALID, GKV_ERR_NOSPACE, GKV_ERR_NOTFOUND, GKV_ERR_DEVICE = 0, 
 GKV_F32, GKV_BF16 = 0, 1
 BACKEND_AUTO, BACKEND_CASCADE, BACKEND_DENSE = 0, 1, 2
 BACKEND_NAMES = {BACKEND_AUTO: "auto", BACKEND_CASCADE: "cascade", BACKEND_DENSE: "dense"}
+PARTIALS_INPUT, PARTIALS_F32 = 0, 1
 
 
 class GkvError(RuntimeError):
@@ -43,7 +44,7 @@ class _Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("hot_capacity_tokens", ctypes.c_int64),
                 ("cold_capacity_tokens", ctypes.c_int64), ("m_sat", ctypes.c_int32),
-                ("force_backend", ctypes.c_int32)]
+                ("force_backend", ctypes.c_int32), ("partials", ctypes.c_int32)]
 
 
 class _Stats(ctypes.Structure):
@@ -58,7 +59,8 @@ class _PlanInfo(ctypes.Structure):
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
                 ("joins_partials", ctypes.c_int32), ("suffix_part_tokens", ctypes.c_int32),
                 ("folded_parts", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double)]
+                ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double),
+                ("host_call_us", ctypes.c_double)]
 
 
 class _PrefixRef(ctypes.Structure):
@@ -111,6 +113,9 @@ SIGNATURES = {
     "gkv_select_backend": (ctypes.c_int, [_P, _I32, _PI32]),
     "gkv_set_dispatch": (ctypes.c_int, [_P, _I32, _I32]),
     "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
+    "gkv_step_status": (ctypes.c_int, [_P, _P, _PI32]),
+    "gkv_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
+    "gkv_set_join_spin_limit": (ctypes.c_int, [_P, _I32]),
     "gkv_kernel_timing": (ctypes.c_int, [_P, _I32]),
     "gkv_kernel_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), _I32, _PI32]),
 }
@@ -145,6 +150,13 @@ def partition_capacity(total_tokens: int, f_p: float = 0.2):
     return hot.value, cold.value
 
 
+def stream_read(dev, nbytes: int, workgroups: int, sink_dev, stream=None):
+    """gkv_stream_read: a plain streaming read of nbytes at dev (measurement)."""
+    rc = load_library().gkv_stream_read(_ptr(dev), nbytes, workgroups, _ptr(sink_dev), _stream(stream))
+    if rc != GKV_OK:
+        raise GkvError(rc, "stream_read: bad arguments or launch failure")
+
+
 def _ptr(x) -> Optional[int]:
     if x is None:
         return None
@@ -171,11 +183,18 @@ class Context:
 
     def __init__(self, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: str,
                  hot_capacity_tokens: int, cold_capacity_tokens: int, n_layers: int = 1,
-                 m_sat: int = 0, force_backend: int = BACKEND_AUTO):
+                 m_sat: int = 0, force_backend: int = BACKEND_AUTO, partial_dtype: str = "input"):
+        """partial_dtype: element type of the step's partial results before
+        their join: "input" (the input dtype, the default), "f32", or "bf16"
+        (bf16 inputs only: the same as "input")."""
         self._lib = load_library()
         self.dtype = dtype
+        if partial_dtype not in ("input", "f32", "bf16") or (partial_dtype == "bf16" and dtype != "bf16"):
+            raise GkvError(GKV_ERR_INVALID, f"partial dtype {partial_dtype!r} with {dtype} inputs")
+        self.partial_dtype = "f32" if partial_dtype == "f32" or dtype == "f32" else "bf16"
         cfg = _Config(n_q_heads, n_kv_heads, head_dim, GKV_BF16 if dtype == "bf16" else GKV_F32,
-                      n_layers, hot_capacity_tokens, cold_capacity_tokens, m_sat, force_backend)
+                      n_layers, hot_capacity_tokens, cold_capacity_tokens, m_sat, force_backend,
+                      PARTIALS_F32 if partial_dtype == "f32" else PARTIALS_INPUT)
         h = _P()
         rc = self._lib.gkv_create(ctypes.byref(cfg), ctypes.byref(h))
         if rc != GKV_OK:
@@ -350,6 +369,16 @@ class Context:
             self._h, ms.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), max_calls, ctypes.byref(n)),
             "kernel_timing_read")
         return ms[:n.value]
+
+    def step_status(self, stream=None) -> int:
+        """gkv_step_status: joins that gave up waiting since the last read
+        (synchronises the stream)."""
+        n = ctypes.c_int32()
+        self._check(self._lib.gkv_step_status(self._h, _stream(stream), ctypes.byref(n)), "step_status")
+        return n.value
+
+    def set_join_spin_limit(self, polls: int):
+        self._check(self._lib.gkv_set_join_spin_limit(self._h, polls), "set_join_spin_limit")
 
     def last_plan(self) -> dict:
         p = _PlanInfo()

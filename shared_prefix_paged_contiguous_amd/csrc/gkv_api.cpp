@@ -20,9 +20,6 @@
 
 namespace {
 
-// M_sat on MI355X: the smallest M_eff from which the dense prefix kernel is
-// never slower than the cascade one, from the dispatcher fit over the
-// Qwen-2.5-14B and Llama-3.1-8B head shapes at L_p = 16K.
 // Dispatcher threshold on M_eff = batch * (query heads per KV head).  Fit on
 // MI355X over full decode steps (Llama-3.1-8B and Qwen-2.5-14B attention
 // shapes, L_p = 16K, suffixes of 128..1024 tokens, M_eff 32..3840): the
@@ -53,6 +50,10 @@ struct gkv_ctx {
   bool ws_clear = false;    // counters of a newly bound workspace still to be zeroed
   int32_t m_sat;
   int32_t force;
+  int32_t spin_limit = gkv::kDefaultSpinLimit;   // join wait bound (polls)
+  bool topo_ready = false;  // device topology read (else the gfx950 defaults plan the step)
+  int32_t dev_cus = gkv::kDefaultCus;
+  int32_t dev_xcds = gkv::kDefaultCus / gkv::kCusPerXcd;
   std::string err;
   gkv::StepArgs args;   // kernel-argument block of the current step (~9 KB)
   std::vector<hipEvent_t> timing_events;   // 2 per recorded call (kernel start, end)
@@ -83,13 +84,17 @@ int device_fail(gkv_ctx* ctx, const char* what, hipError_t e) {
 }
 
 // Arrival counters of the in-kernel join, one per (request, KV head), at the
-// start of the workspace.  Zeroed by the first step on a newly bound
-// workspace; every step leaves them zero again (the join resets its counter).
+// start of the workspace, then the status word in a line of its own.
+// Zeroed by the first step on a newly bound workspace; every step leaves the
+// counters zero again (each join takes its count back off).
 size_t counter_bytes(const gkv_config& c) {
   return gkv::align256(static_cast<size_t>(gkv::kMaxBatch) * c.n_kv_heads * sizeof(int32_t));
 }
+size_t control_bytes(const gkv_config& c) { return counter_bytes(c) + 256; }
 
 size_t elem_size(const gkv_config& c) { return c.dtype == GKV_BF16 ? 2 : 4; }
+// bytes of one element of a partial row (fp32, or the input dtype)
+size_t partial_size(const gkv_config& c) { return c.partials == GKV_PARTIALS_F32 ? 4 : elem_size(c); }
 
 gkv::PlanShape shape_of(const gkv_config& c) {
   return gkv::PlanShape{c.n_q_heads, c.n_kv_heads, c.head_dim, c.dtype == GKV_BF16};
@@ -127,6 +132,7 @@ int gkv_create(const gkv_config* cfg, gkv_ctx** out) {
     return GKV_ERR_INVALID;
   if (c.force_backend < GKV_BACKEND_AUTO || c.force_backend > GKV_BACKEND_DENSE) return GKV_ERR_INVALID;
   if (c.force_backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) return GKV_ERR_INVALID;
+  if (c.partials != GKV_PARTIALS_INPUT && c.partials != GKV_PARTIALS_F32) return GKV_ERR_INVALID;
   gkv_ctx* ctx = new (std::nothrow) gkv_ctx(c);
   if (!ctx) return GKV_ERR_INVALID;
   *out = ctx;
@@ -193,10 +199,10 @@ int gkv_hot_write(gkv_ctx* ctx, int32_t layer, int32_t prefix_id, int32_t token_
 int gkv_workspace_size(const gkv_ctx* ctx, int32_t max_batch, int64_t max_suffix_tokens, size_t* bytes) {
   if (!ctx || !bytes || max_batch < 1 || max_suffix_tokens < 0) return GKV_ERR_INVALID;
   const gkv::PlanShape s = shape_of(ctx->cfg);
-  const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * elem_size(ctx->cfg);   // partial rows: input dtype
+  const size_t row = static_cast<size_t>(ctx->cfg.head_dim) * partial_size(ctx->cfg);
   const int64_t pr = gkv::prefix_rows_bound(s, max_batch);
   const int64_t sr = gkv::suffix_rows_bound(s, max_batch, max_suffix_tokens);
-  *bytes = counter_bytes(ctx->cfg) + gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
+  *bytes = control_bytes(ctx->cfg) + gkv::align256(pr * row) + gkv::align256(pr * 4) + gkv::align256(sr * row) +
            gkv::align256(sr * 4);
   return GKV_OK;
 }
@@ -384,6 +390,42 @@ int gkv_set_dispatch(gkv_ctx* ctx, int32_t force_backend, int32_t m_sat) {
   return GKV_OK;
 }
 
+int gkv_stream_read(const void* dev, size_t bytes, int32_t workgroups, uint32_t* sink_dev, void* stream) {
+  if (!dev || !sink_dev || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dev) % 16 != 0 || workgroups < 1 ||
+      workgroups > (1 << 20))
+    return GKV_ERR_INVALID;
+  if (gkv::launch_stream_read(dev, bytes, workgroups, sink_dev, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GKV_ERR_DEVICE;
+  return GKV_OK;
+}
+
+int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (polls < -1) return fail(ctx, GKV_ERR_INVALID, "spin limit must be >= 0 (or -1 for the default)");
+  ctx->spin_limit = polls == -1 ? gkv::kDefaultSpinLimit : polls;
+  return GKV_OK;
+}
+
+int gkv_step_status(gkv_ctx* ctx, void* stream, int32_t* joins_timed_out) {
+  if (!ctx || !joins_timed_out) return GKV_ERR_INVALID;
+  *joins_timed_out = 0;
+  if (!ctx->ws) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
+  if (ctx->ws_clear) return GKV_OK;   // no step has run on this workspace since it was bound
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t* status =
+      reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(ctx->ws) + counter_bytes(ctx->cfg));
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, status, sizeof(v), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return device_fail(ctx, "status read", e);
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return device_fail(ctx, "status read (stream sync)", e);
+  // a step whose join gave up leaves its counters exact (the join takes its
+  // count off either way); the whole control area is still cleared before
+  // the next step, which also zeroes the status word
+  if (v != 0) ctx->ws_clear = true;
+  *joins_timed_out = v;
+  return GKV_OK;
+}
+
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out) {
   if (!ctx || !out) return GKV_ERR_INVALID;
   if (!ctx->have_last) return GKV_ERR_NOTFOUND;
@@ -438,6 +480,35 @@ int gkv_kernel_timing_read(gkv_ctx* ctx, float* ms, int32_t max_calls, int32_t* 
 
 namespace {
 
+// Compute units and XCDs of the current device, read once per context.  The
+// library is built for gfx950 only; another device is refused.  Without a
+// device (host-only use) the gfx950 values stay and the launch reports the
+// missing device.
+int read_topology(gkv_ctx* ctx) {
+  if (ctx->topo_ready) return GKV_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GKV_OK;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return GKV_OK;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(ctx, GKV_ERR_DEVICE, std::string("libgkv is built for gfx950; device ") + std::to_string(dev) +
+                                         " is " + prop.gcnArchName);
+  const int cus = prop.multiProcessorCount;
+  if (cus < gkv::kCusPerXcd || cus % gkv::kCusPerXcd != 0)
+    return fail(ctx, GKV_ERR_DEVICE, "unexpected compute-unit count " + std::to_string(cus) +
+                                         " (gfx950 XCDs hold " + std::to_string(gkv::kCusPerXcd) + ")");
+  ctx->dev_cus = cus;
+  ctx->dev_xcds = cus / gkv::kCusPerXcd;
+  ctx->topo_ready = true;
+  return GKV_OK;
+}
+
 // The decode step behind gkv_attn_decode (k_new == nullptr) and
 // gkv_decode_step (the batch's new tokens appended inside the launch).
 int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
@@ -446,6 +517,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
                 void* stream, int32_t* backend_out) {
   if (!ctx) return GKV_ERR_INVALID;
   const auto t_start = std::chrono::steady_clock::now();
+  if (int r = read_topology(ctx)) return r;
   if (int r = check_layer(ctx, layer)) return r;
   if (batch < 1) return fail(ctx, GKV_ERR_INVALID, "batch must be >= 1");
   if (!q || !out || !lse || !hot_prefix_ids || !cold_indptr_h)
@@ -477,12 +549,15 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   gkv::Plan plan;
   std::string err;
   gkv::StepArgs& a = ctx->args;
-  if (gkv::build_plan(shape_of(c), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
+  gkv::PlanShape shape = shape_of(c);
+  shape.xcds = ctx->dev_xcds;
+  shape.cus = ctx->dev_cus;
+  if (gkv::build_plan(shape, ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
     return fail(ctx, GKV_ERR_INVALID, err);
 
-  // workspace: [counters][prefix o][prefix lse][suffix o][suffix lse]
-  const size_t row = static_cast<size_t>(c.head_dim) * elem_size(c);   // partial rows: input dtype
-  const size_t off_po = counter_bytes(c);
+  // workspace: [counters][status][prefix o][prefix lse][suffix o][suffix lse]
+  const size_t row = static_cast<size_t>(c.head_dim) * partial_size(c);
+  const size_t off_po = control_bytes(c);
   const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
   const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
   const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
@@ -514,6 +589,9 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   a.v_new = k_new ? v_new : nullptr;
   a.new_slots = k_new ? new_slots_d : nullptr;
   a.counters = reinterpret_cast<int32_t*>(ws);
+  a.status = reinterpret_cast<int32_t*>(ws + counter_bytes(c));
+  a.spin_limit = ctx->spin_limit;
+  a.partial_f32 = partial_size(c) == 4 ? 1 : 0;
   a.p_o = ws + off_po;
   a.p_lse = reinterpret_cast<float*>(ws + off_pl);
   a.s_o = ws + off_so;
@@ -527,11 +605,12 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
     ctx->timing_used++;
   }
   if (ctx->ws_clear) {
-    if ((e = gkv::launch_zero_i32(a.counters, counter_bytes(c) / 4, st)) != hipSuccess)
+    if ((e = gkv::launch_zero_i32(a.counters, control_bytes(c) / 4, st)) != hipSuccess)
       return device_fail(ctx, "counter clear launch", e);
     ctx->ws_clear = false;
   }
   if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);
+  const auto t_launched = std::chrono::steady_clock::now();
 
   ctx->last.backend = backend;
   ctx->last.m_eff = plan.m_eff;
@@ -545,6 +624,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   ctx->last.reserved = 0;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
+  ctx->last.host_call_us = std::chrono::duration<double, std::micro>(t_launched - t_start).count();
   ctx->have_last = true;
   if (backend_out) *backend_out = backend;
   return GKV_OK;

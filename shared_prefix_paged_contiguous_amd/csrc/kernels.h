@@ -27,6 +27,11 @@ hipError_t launch_hot_write(const void* k_rows, const void* v_rows, int32_t n, i
 hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
                        hipEvent_t* ev = nullptr);
 
+// Streaming read of `bytes` (a multiple of 16) at p with `workgroups`
+// workgroups; the data is discarded (sink: dev, 4 bytes, normally untouched).
+hipError_t launch_stream_read(const void* p, size_t bytes, int32_t workgroups, uint32_t* sink,
+                              hipStream_t stream);
+
 // Zeroes n int32 words at p (a fill kernel, so that it can be captured).
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream);
 

@@ -673,11 +673,11 @@ __device__ __forceinline__ void unpack_chunk(const u32x4& w, float (&v)[16 / siz
 // partials is a handful of independent loads issued back to back (indices
 // past the last partial repeat it and weigh zero).  The lane groups then sum
 // their chunks with cross-lane adds.
-template <typename T, int D>
+template <typename T, int D, typename P>
 __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, int b, int h, int lane) {
-  constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
+  constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
   constexpr int RPI = 64 / CH;                                 // rows per wave-wide access
-  constexpr int EPC = 16 / static_cast<int>(sizeof(T));      // values per chunk
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));      // values per chunk
   constexpr int NB = 32;                                       // partials per batch
   constexpr int NL = NB / RPI;                                 // chunk loads per lane per batch
   static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
@@ -689,7 +689,7 @@ __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, 
   };
   auto lse_of = [&](int p) { return load_partial((p < ns ? a.p_lse : a.s_lse) + row_of(p)); };
   auto chunk_of = [&](int p) {
-    const T* base = static_cast<const T*>(p < ns ? a.p_o : a.s_o);
+    const P* base = static_cast<const P*>(p < ns ? a.p_o : a.s_o);
     return load_partial_chunk(base + row_of(p) * D + EPC * ch);
   };
   auto wave_max = [](float x) {
@@ -720,7 +720,7 @@ __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, 
     for (int i = 0; i < NL; ++i) {
       const float w = __shfl(wl, i * RPI + rg);   // zero for rows past cnt
       float v[EPC];
-      unpack_chunk<T>(raw[i], v);
+      unpack_chunk<P>(raw[i], v);
 #pragma unroll
       for (int j = 0; j < EPC; ++j) acc[j] += w * v[j];
     }
@@ -753,22 +753,32 @@ __device__ __forceinline__ void arrive(const StepArgs& a, int b, int g) {
                          __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Most polls of an arrival counter before a join gives up.  A poll is an
-// agent-scope load plus a short sleep (about a microsecond), so the bound
-// (~0.1 s) is far beyond any step's duration; it only guarantees that the
-// kernel ends even if a count were never to arrive (the join then reads
-// whatever the partials hold).
-constexpr int kSpinLimit = 1 << 16;
-
 // Waits until all n partials of (request b, KV head g) have arrived, then
-// rewinds the counter to zero for the next call.  One thread calls it.
+// takes n off the counter for the next call.  One thread calls it.
+//
+// The wait is bounded by a.spin_limit polls (an agent-scope load plus a short
+// sleep each; the default bound, about 0.1 s, is far beyond any step), so the
+// kernel ends even if a count were never to arrive.  A join that stops
+// waiting adds one to the workspace's status word (read by the host with
+// gkv_step_status) and joins whatever the partials hold; its output is not
+// valid.  Taking n off (instead of storing zero) keeps the counters exact
+// for the next call in that case too: the late arrivals of this call still
+// land before the kernel ends, and bring the counter back to zero.
 __device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, int n) {
   int32_t* cnt = a.counters + static_cast<size_t>(b) * a.n_kv + g;
-  for (int it = 0; it < kSpinLimit; ++it) {
-    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
+  bool arrived = false;
+  for (int it = 0; it < a.spin_limit; ++it) {
+    if (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) {
+      arrived = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
   }
-  __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!arrived) {
+    arrived = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n;
+    if (!arrived) __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_fetch_add(cnt, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------ suffix blocks
@@ -821,7 +831,7 @@ __device__ __forceinline__ SuffixPiece suffix_piece(const StepArgs& a, int part,
 // wave w joins columns w, w+4, ... and writes the request's output (a
 // request without a HOT prefix whose slot table is this one part) or the
 // part's partial.  Returns true for the former.
-template <typename T, int D>
+template <typename T, int D, typename P>
 __device__ __forceinline__ bool suffix_publish(const StepArgs& a, SuffixSmem<T, D>& sm, int part, int b,
                                                bool single, int gk, int wave, int lane) {
   constexpr int PER = D / 64;
@@ -844,7 +854,7 @@ __device__ __forceinline__ bool suffix_publish(const StepArgs& a, SuffixSmem<T, 
       if (lane == 0) a.lse[static_cast<size_t>(b) * a.n_q + hc] = l2 * 0.69314718055994531f;
     } else {
       const size_t row = static_cast<size_t>(part) * a.n_q + hc;
-      store_partial_vals<T, PER>(static_cast<T*>(a.s_o) + row * D + PER * lane, acc);
+      store_partial_vals<P, PER>(static_cast<P*>(a.s_o) + row * D + PER * lane, acc);
       if (lane == 0) store_partial(a.s_lse + row, l2);
     }
   }
@@ -883,7 +893,7 @@ __device__ __forceinline__ void suffix_copy_new(const StepArgs& a, int b, int gk
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, typename P>
 __device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
@@ -1015,7 +1025,7 @@ __device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk,
   // the wave pieces meet in LDS
   suffix_to_lds<T, D>(sm, wave, n, g, col_ok, o, lse2);
   __syncthreads();
-  if (suffix_publish<T, D>(a, sm, part, b, single, gk, wave, lane)) return;
+  if (suffix_publish<T, D, P>(a, sm, part, b, single, gk, wave, lane)) return;
 
   // this part's partial is written: count it for the request's join
   wait_stores();
@@ -1026,17 +1036,17 @@ __device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk,
 // Suffix block i: part q = i / n_kv for KV head i % n_kv, or, folded, part
 // n_parts-1-q (the shorter) and then part q; the barrier between the two
 // frees the LDS.  Folded, blocks q >= ceil(n_parts / 2) are grid padding.
-template <typename T, int D>
+template <typename T, int D, typename P>
 __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   const int q = blk / a.n_kv;
   const int gk = blk - q * a.n_kv;
   if (q >= (a.fold ? (a.n_parts + 1) / 2 : a.n_parts)) return;   // grid padding
   const int first = a.fold ? a.n_parts - 1 - q : q;
   if (first > q) {
-    suffix_part<T, D>(a, first, gk, smem_raw);
+    suffix_part<T, D, P>(a, first, gk, smem_raw);
     __syncthreads();
   }
-  suffix_part<T, D>(a, q, gk, smem_raw);
+  suffix_part<T, D, P>(a, q, gk, smem_raw);
 }
 
 // ------------------------------------------------------------ prefix kernel
@@ -1117,15 +1127,23 @@ __device__ __forceinline__ void wait_blocks_after(int n) {
 // explicit vmcnt waits, and the compiler's conservative view of them would
 // otherwise drain the whole ring at some loop barriers.  The compiler's
 // waits for other loads stay correct, only more conservative: vector loads
-// retire in issue order.
+// retire in issue order.  The copy takes its LDS address from M0, a
+// register the compiler may hold a value in (it cannot be declared
+// clobbered): the asm saves M0 in a scratch SGPR and restores it, and the
+// trailing s_nop covers the wait state an M0 write needs before an
+// instruction that reads it.
 __device__ __forceinline__ void load_lds_1k(uint32_t voff, const uint8_t* base, uint32_t lds) {
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0"
+      : "=&s"(saved)
       : "v"(voff), "s"(base), "s"(lds)
-      : "memory", "m0");
+      : "memory");
 }
 
 // LDS byte address of a pointer into __shared__ memory
@@ -1158,7 +1176,7 @@ struct PrefixSmem {
   uint8_t ring[kStages][2 * kImg];
 };
 
-template <typename T, int D, int RB>
+template <typename T, int D, int RB, typename P>
 __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
@@ -1175,9 +1193,10 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   }
   const ClassDesc& cl = a.classes[ci];
   const int local = blk - cl.block_base;
-  const int r8 = local / kXcds;
+  const int xcds = a.xcds;
+  const int r8 = local / xcds;
   const int m_tile = r8 % cl.m_tiles;
-  const int grp = (r8 / cl.m_tiles) * kXcds + local % kXcds;
+  const int grp = (r8 / cl.m_tiles) * xcds + local % xcds;
   if (grp >= cl.n_groups) return;   // XCD padding: whole workgroup leaves before any barrier
   const int kv_head = grp / cl.n_splits, split = grp % cl.n_splits;
   const int t0 = split * cl.chunk;
@@ -1399,7 +1418,7 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       // 16-byte stores: lane l writes chunk l % CH of row l / CH of each
       // group of RPI rows, so one instruction covers RPI whole rows.  All
       // chunks leave LDS before the first store (one LDS wait).
-      constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;
+      constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;
       constexpr int RPI = 64 / CH;
       static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
       const int ch = lane % CH, rsub = lane / CH;
@@ -1408,13 +1427,13 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
 #pragma unroll
       for (int s = 0; s < 16 / RPI; ++s) {
         const int rr = s * RPI + rsub;
-        pk[s] = pack_chunk<T>(stage + rr * kStride + (16 / sizeof(T)) * ch);
+        pk[s] = pack_chunk<P>(stage + rr * kStride + (16 / sizeof(P)) * ch);
         prow_of[s] = __shfl(prow, rr);
       }
 #pragma unroll
       for (int s = 0; s < 16 / RPI; ++s)
         if (wrow0 + 16 * rb + s * RPI + rsub < rows)
-          store_chunk(static_cast<T*>(a.p_o) + static_cast<size_t>(prow_of[s]) * D + (16 / sizeof(T)) * ch, pk[s],
+          store_chunk(static_cast<P*>(a.p_o) + static_cast<size_t>(prow_of[s]) * D + (16 / sizeof(P)) * ch, pk[s],
                       a.narrow_ws != 0);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -1449,7 +1468,7 @@ constexpr size_t step_smem_bytes() {
 // then wave w joins the request's query heads g*G + w, g*G + w + 4, ...
 // Where the partials lie is read before the wait, so after it only the
 // partials themselves are loaded.
-template <typename T, int D>
+template <typename T, int D, typename P>
 __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
   const int b = j / a.n_kv, g = j - (j / a.n_kv) * a.n_kv;
   const JoinSrc src = join_src(a, b);
@@ -1458,10 +1477,10 @@ __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
   if (threadIdx.x == 0) wait_arrivals(a, b, g, n);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int col = wave; col < a.group; col += kWaves) join_row<T, D>(a, src, b, g * a.group + col, lane);
+  for (int col = wave; col < a.group; col += kWaves) join_row<T, D, P>(a, src, b, g * a.group + col, lane);
 }
 
-template <typename T, int D, int RB>
+template <typename T, int D, int RB, typename P>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
@@ -1469,11 +1488,11 @@ void step_kernel(StepArgs a) {
   const int blk = blockIdx.x;
   const int work = a.prefix_blocks + a.suffix_blocks;
   if (blk >= work) {
-    join_block<T, D>(a, blk - work);
+    join_block<T, D, P>(a, blk - work);
     return;
   }
-  if (blk < a.prefix_blocks) prefix_block<T, D, RB>(a, blk, smem);
-  else suffix_block<T, D>(a, blk - a.prefix_blocks, smem);
+  if (blk < a.prefix_blocks) prefix_block<T, D, RB, P>(a, blk, smem);
+  else suffix_block<T, D, P>(a, blk - a.prefix_blocks, smem);
 }
 
 __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, const u32x4* v_new,
@@ -1498,16 +1517,47 @@ hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, 
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
   const int blocks = a.prefix_blocks + a.suffix_blocks + a.join_blocks;
   (void)backend;
-  if (a.rb == 2) {
-    if constexpr (sizeof(T) == 2) {
-      hipExtLaunchKernelGGL(step_kernel<T, D, 2>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+  if constexpr (sizeof(T) == 2) {
+    // bf16 inputs: partial rows in fp32 or in bf16, 64- or 128-row prefix tiles
+    if (a.partial_f32) {
+      if (a.rb == 2)
+        hipExtLaunchKernelGGL(step_kernel<T, D, 2, float>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+      else
+        hipExtLaunchKernelGGL(step_kernel<T, D, 1, float>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     } else {
-      return hipErrorInvalidValue;
+      if (a.rb == 2)
+        hipExtLaunchKernelGGL(step_kernel<T, D, 2, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+      else
+        hipExtLaunchKernelGGL(step_kernel<T, D, 1, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     }
   } else {
-    hipExtLaunchKernelGGL(step_kernel<T, D, 1>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+    // fp32 inputs: fp32 partials, 64-row tiles
+    if (a.rb != 1 || !a.partial_f32) return hipErrorInvalidValue;
+    hipExtLaunchKernelGGL(step_kernel<T, D, 1, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
   }
   return hipGetLastError();
+}
+
+// Streaming read of n16 16-byte vectors (the measured read ceiling of the
+// device): consecutive lanes read consecutive vectors, eight loads in flight
+// per lane, and the data only feeds an xor whose (practically never taken)
+// store to `sink` keeps the loads alive.
+__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* p, int64_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = p[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = p[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
 }
 
 __global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* p, size_t n) {
@@ -1522,6 +1572,13 @@ hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const int grid = static_cast<int>(std::min<size_t>((n + kThreads - 1) / kThreads, 1024));
   zero_kernel<<<grid, kThreads, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* p, size_t bytes, int32_t workgroups, uint32_t* sink, hipStream_t stream) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  read_kernel<<<workgroups, kThreads, 0, stream>>>(static_cast<const u32x4*>(p), n16, sink);
   return hipGetLastError();
 }
 

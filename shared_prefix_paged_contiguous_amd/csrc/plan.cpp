@@ -32,6 +32,9 @@ int64_t suffix_rows_bound(const PlanShape& s, int32_t max_batch, int64_t max_suf
 int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const int32_t* ids,
                const int32_t* indptr, int32_t backend, StepArgs& a, Plan& plan, std::string& err) {
   const int32_t n_q = shape.n_q, n_kv = shape.n_kv, group = n_q / n_kv;
+  const int32_t xcds = std::max(1, shape.xcds);
+  const int64_t step_slots = static_cast<int64_t>(kWgsPerCu) * std::max(1, shape.cus);
+  const int64_t pad = static_cast<int64_t>(kGroupPerXcd) * xcds;   // padding unit of the grid ranges
   plan = Plan();
   plan.backend = backend;
   plan.m_eff = batch * group;
@@ -147,11 +150,11 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
       cd.m_tiles = static_cast<int32_t>(ceil_div(cd.n_members, tm));
       cd.n_groups = n_kv * cd.n_splits;
       cd.block_base = nb;
-      cd.n_blocks = kXcds * static_cast<int32_t>(ceil_div(cd.n_groups, kXcds)) * cd.m_tiles;
+      cd.n_blocks = xcds * static_cast<int32_t>(ceil_div(cd.n_groups, xcds)) * cd.m_tiles;
       cd.pad_ = 0;
       nb += cd.n_blocks;
     }
-    return static_cast<int32_t>(round_up(nb, kGroup));
+    return static_cast<int32_t>(round_up(nb, pad));
   };
   const int64_t split0 = std::max<int64_t>(
       kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), target), kPrefixTile));
@@ -164,16 +167,16 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     for (int32_t b = 0; b < batch; ++b)
       parts += std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
     const int64_t pairs = ceil_div(parts, 2) * n_kv;
-    if (parts > 1 && parts * n_kv > kStepSlots - blocks && pairs > kStepSlots - blocks &&
-        pairs <= kStepSlots - kGroup) {
+    if (parts > 1 && parts * n_kv > step_slots - blocks && pairs > step_slots - blocks &&
+        pairs <= step_slots - pad) {
       int64_t st = split0 + kPrefixTile;
-      while (st <= 2 * split0 && split_classes(st) > kStepSlots - pairs) st += kPrefixTile;
+      while (st <= 2 * split0 && split_classes(st) > step_slots - pairs) st += kPrefixTile;
       blocks = split_classes(st <= 2 * split0 ? st : split0);   // the classes keep the last call's splits
     }
   }
   int32_t max_splits = 0;
   for (int32_t c = 0; c < n_classes; ++c) max_splits = std::max(max_splits, a.classes[c].n_splits);
-  a.prefix_blocks = static_cast<int32_t>(round_up(blocks, kGroup));
+  a.prefix_blocks = static_cast<int32_t>(round_up(blocks, pad));
   a.max_splits = max_splits;
   plan.prefix_blocks = a.prefix_blocks;
   plan.prefix_rows = static_cast<int64_t>(batch) * max_splits * n_q;
@@ -195,7 +198,7 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
     if (np > 1) multi = 1;
     parts += np;
   }
-  if ((parts + kGroup) * n_kv + static_cast<int64_t>(batch) * n_kv + blocks > 0x7fffffffLL) {
+  if ((parts + pad) * n_kv + static_cast<int64_t>(batch) * n_kv + blocks > 0x7fffffffLL) {
     err = "too many suffix parts";
     return -1;
   }
@@ -205,12 +208,12 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   // prefix leaves and the folded ones fit (cascade steps only: dense fills
   // every slot with prefix work).  Folding into a second round of paired
   // workgroups is slower than not folding.
-  const int64_t free_slots = kStepSlots - static_cast<int64_t>(a.prefix_blocks);
+  const int64_t free_slots = step_slots - static_cast<int64_t>(a.prefix_blocks);
   const bool fold = backend == GKV_BACKEND_CASCADE && parts > 1 && parts * n_kv > free_slots &&
                     ceil_div(parts, 2) * n_kv <= free_slots;
   a.fold = fold ? 1 : 0;
-  a.pad1_ = 0;
-  a.suffix_blocks = static_cast<int32_t>(round_up((fold ? ceil_div(parts, 2) : parts) * n_kv, kGroup));
+  a.xcds = xcds;
+  a.suffix_blocks = static_cast<int32_t>(round_up((fold ? ceil_div(parts, 2) : parts) * n_kv, pad));
   plan.fold = a.fold;
   a.multi_part = multi;
   a.need_merge = multi || n_classes > 0;

@@ -20,6 +20,8 @@ namespace gkv {
 struct PlanShape {
   int32_t n_q, n_kv, head_dim;
   bool bf16;
+  int32_t xcds = kDefaultCus / kCusPerXcd;   // XCDs of the device
+  int32_t cus = kDefaultCus;                  // compute units of the device
 };
 
 struct Plan {

@@ -32,8 +32,13 @@ constexpr int kSuffixPart = kWaves * kWaveTokens;   // tokens per suffix workgro
 constexpr int kMaxSplits = 64;    // L splits per prefix class
 constexpr int kHotBlock = 32;     // tokens per HOT block; slabs start on block boundaries
 constexpr int kRingBytes = 64 * 1024;   // LDS ring of a prefix workgroup (K+V images of 3..8 blocks)
-constexpr int kXcds = 8;          // MI355X: workgroups go to the 8 XCDs round-robin
-constexpr int kStepSlots = 512;   // MI355X: 256 CUs x 2 resident step workgroups
+// Chip topology the planner works with (read from the device when a step is
+// planned; these are the gfx950 values used when no device answers, so that
+// host-side validation runs without a GPU).  Workgroups are dealt to the
+// XCDs round-robin by index; each CU holds two step workgroups.
+constexpr int kCusPerXcd = 32;          // gfx950: compute units per XCD
+constexpr int kDefaultCus = 256;        // MI355X: 8 XCDs x 32 CUs
+constexpr int kWgsPerCu = 2;            // resident step workgroups per CU
 
 // Requests per prefix M-tile: a tile holds whole requests (all G query
 // heads of a member for the tile's KV head), at most 64 * RB rows.
@@ -45,9 +50,10 @@ constexpr int kMaxClasses = 64;
 
 // One distinct HOT prefix in the step ("class": every request that starts
 // with this slab).  Its prefix blocks are [block_base, block_base+n_blocks):
-// local block i -> XCD slot x = i % 8, r = i / 8, M-tile r % m_tiles, group
-// (r / m_tiles) * 8 + x, group = kv_head * n_splits + split.  The M-tiles of
-// one group thus share an XCD (and its L2) and are dispatched together.
+// local block i -> XCD slot x = i % X, r = i / X, M-tile r % m_tiles, group
+// (r / m_tiles) * X + x (X = the device's XCDs), group = kv_head * n_splits
+// + split.  The M-tiles of one group thus share an XCD (and its L2) and are
+// dispatched together.
 struct ClassDesc {
   int64_t slab_off;     // token offset of the slab in the HOT pool
   int32_t len;          // slab length L_c (tokens)
@@ -58,7 +64,7 @@ struct ClassDesc {
   int32_t m_tiles;      // ceil(n_members / tile_members(G, RB)): M-tiles hold whole requests
   int32_t n_groups;     // n_kv * n_splits
   int32_t block_base;   // first prefix block
-  int32_t n_blocks;     // 8 * ceil(n_groups / 8) * m_tiles
+  int32_t n_blocks;     // X * ceil(n_groups / X) * m_tiles
   int32_t pad_;
 };
 
@@ -86,7 +92,8 @@ struct ClassDesc {
 // Grid: prefix blocks, then suffix blocks, then batch * n_kv join blocks.
 // Prefix and suffix blocks never wait, and every join block follows all of
 // them in each XCD's (in-order) dispatch, so the joins' waits end.
-constexpr int kGroup = 4 * kXcds;   // padding unit of the prefix and suffix ranges
+// The prefix and suffix ranges of the grid are padded to 4 * xcds blocks.
+constexpr int kGroupPerXcd = 4;
 
 // A ranked request's suffix work in one 16-byte record (one scalar load).
 struct RankDesc {
@@ -98,10 +105,12 @@ struct RankDesc {
 struct StepArgs {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
+  int32_t xcds;                // XCDs of the device (prefix blocks of one group share one)
+  int32_t spin_limit;          // most polls of a join's wait before it gives up (and reports it)
   int32_t n_classes;
   int32_t rb;                  // row blocks per wave of the prefix tiles (1 or 2)
-  int32_t prefix_blocks;       // sum of class n_blocks, padded to a multiple of kGroup
-  int32_t suffix_blocks;       // n_parts * n_kv, padded to a multiple of kGroup
+  int32_t prefix_blocks;       // sum of class n_blocks, padded to a multiple of 4 * xcds
+  int32_t suffix_blocks;       // n_parts * n_kv (or folded pairs), padded to a multiple of 4 * xcds
   int32_t join_blocks;         // batch * n_kv when some output is joined, else 0
   int32_t max_splits;          // prefix partial row (b, s, h) = (b * max_splits + s) * n_q + h
   int32_t multi_part;          // some request has more than one suffix part
@@ -109,7 +118,7 @@ struct StepArgs {
   int32_t need_merge;          // some request is joined from several partials (HOT prefix or parts)
   int32_t narrow_ws;           // the step's workspace spans less than 2 GB (32-bit store offsets)
   int32_t fold;                // suffix block i runs parts n_parts-1-i/n_kv and i/n_kv (see above)
-  int32_t pad1_;
+  int32_t partial_f32;         // partial rows are fp32 (else the input dtype)
   const void* q;
   void* out;
   float* lse;
@@ -127,11 +136,12 @@ struct StepArgs {
   const void* k_new;
   const void* v_new;
   const int32_t* new_slots;    // dev [B]
-  void* p_o;                   // prefix partials [rows][head_dim], normalised, in the input dtype
+  void* p_o;                   // prefix partials [rows][head_dim], normalised (fp32 or the input dtype)
   float* p_lse;                // prefix partial log2-sum-exp2 of scaled scores
-  void* s_o;                   // suffix-part partials, row = part * n_q + h (input dtype)
+  void* s_o;                   // suffix-part partials, row = part * n_q + h (same dtype as p_o)
   float* s_lse;
   int32_t* counters;           // [kMaxBatch][n_kv] partial arrivals (zero between calls)
+  int32_t* status;             // status word: joins that gave up waiting (see kStatus*)
   ClassDesc classes[kMaxClasses];
   alignas(16) RankDesc ranks[kMaxBatch];   // by rank
   // small-int tables, 4-byte aligned so entries can be read with 32-bit loads
@@ -143,5 +153,10 @@ struct StepArgs {
   int32_t tail;
 };
 constexpr int32_t kArgsTail = 0x47'4b'56'31;
+
+// Status word of a workspace (one 256-byte line after the counters): the
+// number of joins that stopped waiting for their partials at the spin limit
+// (their outputs are not valid).  Zero while every step is well formed.
+constexpr int kDefaultSpinLimit = 1 << 16;
 
 }  // namespace gkv

@@ -53,11 +53,41 @@ def place_through_registry(w: workloads.Workload, ctx: binding.Context):
     return out
 
 
+def paged_copies(ctx: binding.Context, layer: int, prefix_k, prefix_v, cur_k, cur_v, page: int,
+                 rng: np.random.Generator, base_slot: int = 0):
+    """The uniform-page layout of a shared prefix (the baseline the pages
+    compare the HOT slab with): every request gets a copy of its own of the
+    prefix in pages of `page` consecutive COLD slots, the pages in random
+    order, followed by one slot holding the request's current token.
+
+    prefix_k/v: dev [L, n_kv, d] (L a multiple of `page`); cur_k/v: dev
+    [B, n_kv, d].  Writes the rows with gkv_cold_append into slots
+    [base_slot, base_slot + B * (L + 1)) of `layer` and returns the CSR slot
+    table (indptr [B+1] int32 host, indices int32 host), request b's table
+    being its L prefix slots in token order, then its current-token slot."""
+    plen = int(prefix_k.shape[0])
+    bsz = int(cur_k.shape[0])
+    if plen % page:
+        raise ValueError("prefix length must be a whole number of pages")
+    per = plen // page
+    pages = rng.permutation(bsz * per).astype(np.int64)
+    tables = []
+    for b in range(bsz):
+        slots = base_slot + (pages[b * per:(b + 1) * per, None] * page + np.arange(page)[None, :]).reshape(-1)
+        ctx.cold_append(layer, prefix_k, prefix_v, torch.from_numpy(slots.astype(np.int32)).to(prefix_k.device))
+        tables.append(np.concatenate([slots, [base_slot + bsz * plen + b]]).astype(np.int32))
+    cur = torch.arange(base_slot + bsz * plen, base_slot + bsz * plen + bsz, dtype=torch.int32,
+                       device=prefix_k.device)
+    ctx.cold_append(layer, cur_k, cur_v, cur)
+    indptr = (np.arange(bsz + 1, dtype=np.int64) * (plen + 1)).astype(np.int32)
+    return indptr, np.concatenate(tables)
+
+
 class DecodeState:
     def __init__(self, w: workloads.Workload, device: str = "cuda", n_layers: int = 1,
                  m_sat: int = 0, force_backend: int = binding.BACKEND_AUTO,
                  hot_capacity: Optional[int] = None, cold_capacity: Optional[int] = None,
-                 registry: bool = False):
+                 registry: bool = False, partial_dtype: str = "input"):
         s = w.spec
         self.w = w
         self.device = device
@@ -66,7 +96,8 @@ class DecodeState:
         self.cold_cap = s.cold_capacity if cold_capacity is None else cold_capacity
         self.n_layers = n_layers
         self.ctx = binding.Context(s.n_q, s.n_kv, s.head_dim, s.dtype, self.hot_cap, self.cold_cap,
-                                   n_layers=n_layers, m_sat=m_sat, force_backend=force_backend)
+                                   n_layers=n_layers, m_sat=m_sat, force_backend=force_backend,
+                                   partial_dtype=partial_dtype if s.dtype == "bf16" else "input")
         ctx = self.ctx
 
         def hot_alloc(n):

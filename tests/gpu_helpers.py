@@ -9,8 +9,10 @@ import torch
 from oracle.attention import decode_step
 
 # The gate: elementwise |x - r| <= ATOL + RTOL * |r| on out and lse (bf16
-# inputs, fp32 accumulation, bf16 output).
+# inputs, fp32 accumulation, bf16 output), and on its own max |out - ref| <=
+# MAX_ABS (the stated bound on the absolute error).
 ATOL, RTOL = 1e-2, 2e-2
+MAX_ABS = 1e-2
 # Diagnostics held as well (the gate alone is weak when outputs are ~1e-2).
 NORM_REL_MAX = 1e-2       # ||out - ref||_2 / ||ref||_2
 LSE_ABS_MAX = 1e-3
@@ -29,7 +31,7 @@ def oracle_ref(w, requests=None):
 
 
 def check(out, lse, ref_out, ref_lse, requests=None, atol=ATOL, rtol=RTOL,
-          norm_rel=NORM_REL_MAX, lse_abs=LSE_ABS_MAX):
+          norm_rel=NORM_REL_MAX, lse_abs=LSE_ABS_MAX, max_abs=MAX_ABS):
     o = f64(out)
     l = f64(lse)
     if requests is not None:
@@ -47,6 +49,7 @@ def check(out, lse, ref_out, ref_lse, requests=None, atol=ATOL, rtol=RTOL,
     }
     assert not bad_o.any(), f"out outside the gate at {np.argwhere(bad_o)[:5].tolist()} {stats}"
     assert not bad_l.any(), f"lse outside the gate at {np.argwhere(bad_l)[:5].tolist()} {stats}"
+    assert stats["max_abs_out"] <= max_abs, stats
     assert stats["norm_rel_out"] <= norm_rel, stats
     assert stats["max_abs_lse"] <= lse_abs, stats
     return stats

@@ -55,7 +55,8 @@ def test_create_rejects_bad_configs():
     _lib_or_skip()
     for kw in [dict(n_q_heads=10, n_kv_heads=4), dict(head_dim=96), dict(n_q_heads=34, n_kv_heads=2),
                dict(n_q_heads=264, n_kv_heads=33), dict(hot_capacity_tokens=-1), dict(cold_capacity_tokens=2 ** 31),
-               dict(dtype="f32", force_backend=binding.BACKEND_DENSE)]:
+               dict(dtype="f32", force_backend=binding.BACKEND_DENSE), dict(dtype="f32", partial_dtype="bf16"),
+               dict(partial_dtype="f16")]:
         with pytest.raises(binding.GkvError):
             _ctx(**kw)
 
@@ -193,6 +194,18 @@ def test_workload_placement_bit_exact_vs_models(name):
     if name == "hetero8":
         # churn left holes: some slab landed below the running sum of lengths
         assert min(o for o in a["prefix_offset"] if o >= 0) < sum(w.hot_churn[:1])
+
+
+def test_step_status_and_spin_limit_host_checks():
+    c = _ctx()
+    with pytest.raises(binding.GkvError, match="no workspace"):
+        c.step_status(stream=0)
+    c.bind_workspace(256, 1 << 20)
+    assert c.step_status(stream=0) == 0        # nothing has run on the workspace yet: no device call
+    c.set_join_spin_limit(0)
+    c.set_join_spin_limit(-1)
+    with pytest.raises(binding.GkvError):
+        c.set_join_spin_limit(-2)
 
 
 def test_dispatch_rule_matches_model_and_pages():
