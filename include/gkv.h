@@ -314,6 +314,27 @@ int gkv_decode_step(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_ne
                     const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
                     void* stream, int32_t* backend_out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as gkv_decode_step, with the same arguments and result, whose scratch
+ * (join counters, status word, partial results) lives in a static device
+ * array of the library - 32 MiB on every device the library runs on, held
+ * until the process ends - instead of the context's bound workspace, so no
+ * workspace needs to be bound.  Allocates nothing: no hipMalloc, hipFree or
+ * allocating library call.  The first call on a device clears the array's
+ * counters and status word with a small fill kernel on `stream`; every call
+ * leaves the counters at zero again.  GKV_ERR_INVALID (nothing enqueued) if
+ * the step's partial results do not fit the array, besides the errors of
+ * gkv_decode_step.  All calls on one device share its array, whatever their
+ * context: calls that overlap in time on one device (other streams, other
+ * threads) race on it and give undefined results; issue them on one stream.
+ * gkv_step_status also reports joins of these calls that gave up waiting,
+ * from the current device's array. */
+int gkv_decode_step_static(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
+                           const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
+                           void* stream, int32_t* backend_out);
+
 /* Per-step rule alone (host, no GPU): backend for a batch of `batch` requests
  * under the context's threshold and override (paperlayer.ai §3 "Per-step
  * dispatch": dense iff M_eff = B * n_q/n_kv >= M_sat). */

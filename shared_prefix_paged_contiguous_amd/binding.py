@@ -110,6 +110,7 @@ SIGNATURES = {
     "gkv_cold_append": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _P]),
     "gkv_attn_decode": (ctypes.c_int, [_P, _I32, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P, _P]),
     "gkv_decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P]),
+    "gkv_decode_step_static": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _PI32, _PI32, _P, _P, _P, _P, _P]),
     "gkv_select_backend": (ctypes.c_int, [_P, _I32, _PI32]),
     "gkv_set_dispatch": (ctypes.c_int, [_P, _I32, _I32]),
     "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
@@ -347,6 +348,21 @@ class Context:
             self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_slots_dev), batch,
             ids.ctypes.data_as(_PI32), ind.ctypes.data_as(_PI32), _ptr(cold_indices_d), _ptr(out), _ptr(lse),
             _stream(stream), ctypes.byref(backend)), "decode_step")
+        return backend.value
+
+    def decode_step_static(self, layer: int, q, k_new, v_new, new_slots_dev, hot_prefix_ids, cold_indptr_h,
+                           cold_indices_d, out, lse, batch: Optional[int] = None, stream=None) -> int:
+        """gkv_decode_step_static: decode_step with its scratch in the
+        library's static device array (no workspace, no allocation)."""
+        ids = _i32(hot_prefix_ids)
+        ind = _i32(cold_indptr_h)
+        if batch is None:
+            batch = len(ids)
+        backend = ctypes.c_int32()
+        self._check(self._lib.gkv_decode_step_static(
+            self._h, layer, _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(new_slots_dev), batch,
+            ids.ctypes.data_as(_PI32), ind.ctypes.data_as(_PI32), _ptr(cold_indices_d), _ptr(out), _ptr(lse),
+            _stream(stream), ctypes.byref(backend)), "decode_step_static")
         return backend.value
 
     # ------------------------------------------------------------ dispatcher

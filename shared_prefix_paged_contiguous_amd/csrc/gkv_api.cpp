@@ -61,6 +61,7 @@ struct gkv_ctx {
   int32_t timing_used = 0;
   gkv_plan_info last{};
   bool have_last = false;
+  int32_t static_device = -1;   // device of the last allocation-free step (its scratch holds a status word)
 
   explicit gkv_ctx(const gkv_config& c)
       : cfg(c),
@@ -409,20 +410,46 @@ int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls) {
 int gkv_step_status(gkv_ctx* ctx, void* stream, int32_t* joins_timed_out) {
   if (!ctx || !joins_timed_out) return GKV_ERR_INVALID;
   *joins_timed_out = 0;
-  if (!ctx->ws) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
-  if (ctx->ws_clear) return GKV_OK;   // no step has run on this workspace since it was bound
+  if (!ctx->ws && ctx->static_device < 0) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t* status =
-      reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(ctx->ws) + counter_bytes(ctx->cfg));
-  int32_t v = 0;
-  hipError_t e = hipMemcpyAsync(&v, status, sizeof(v), hipMemcpyDeviceToHost, st);
-  if (e != hipSuccess) return device_fail(ctx, "status read", e);
-  if ((e = hipStreamSynchronize(st)) != hipSuccess) return device_fail(ctx, "status read (stream sync)", e);
-  // a step whose join gave up leaves its counters exact (the join takes its
-  // count off either way); the whole control area is still cleared before
-  // the next step, which also zeroes the status word
-  if (v != 0) ctx->ws_clear = true;
-  *joins_timed_out = v;
+  int32_t total = 0;
+  auto read_word = [&](const int32_t* status, int32_t* v) -> int {
+    hipError_t e = hipMemcpyAsync(v, status, sizeof(*v), hipMemcpyDeviceToHost, st);
+    if (e != hipSuccess) return device_fail(ctx, "status read", e);
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return device_fail(ctx, "status read (stream sync)", e);
+    return GKV_OK;
+  };
+  if (ctx->ws && !ctx->ws_clear) {   // else no step has run on this workspace since it was bound
+    int32_t v = 0;
+    if (int r = read_word(reinterpret_cast<const int32_t*>(static_cast<const uint8_t*>(ctx->ws) +
+                                                           counter_bytes(ctx->cfg)), &v))
+      return r;
+    // a step whose join gave up leaves its counters exact (the join takes its
+    // count off either way); the whole control area is still cleared before
+    // the next step, which also zeroes the status word
+    if (v != 0) ctx->ws_clear = true;
+    total += v;
+  }
+  if (ctx->static_device >= 0) {   // the static scratch of the current device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_fail(ctx, "hipGetDevice", e);
+    uint8_t* p = nullptr;
+    bool first = false;
+    if ((e = gkv::scratch_region(dev, &p, &first)) != hipSuccess)
+      return device_fail(ctx, "static scratch address (hipGetSymbolAddress)", e);
+    if (first) {   // never used on this device: clear it for its first step
+      if ((e = gkv::launch_zero_i32(reinterpret_cast<int32_t*>(p), gkv::kStaticControlBytes / 4, st)) != hipSuccess)
+        return device_fail(ctx, "scratch clear launch", e);
+    } else {
+      int32_t v = 0;
+      if (int r = read_word(reinterpret_cast<const int32_t*>(p), &v)) return r;
+      if (v != 0 && (e = gkv::launch_zero_i32(reinterpret_cast<int32_t*>(p), 1, st)) != hipSuccess)
+        return device_fail(ctx, "status clear launch", e);
+      total += v;
+    }
+  }
+  *joins_timed_out = total;
   return GKV_OK;
 }
 
@@ -509,12 +536,14 @@ int read_topology(gkv_ctx* ctx) {
   return GKV_OK;
 }
 
-// The decode step behind gkv_attn_decode (k_new == nullptr) and
-// gkv_decode_step (the batch's new tokens appended inside the launch).
+// The decode step behind gkv_attn_decode (k_new == nullptr), gkv_decode_step
+// (the batch's new tokens appended inside the launch) and
+// gkv_decode_step_static (the same, its scratch in the library's static
+// device array instead of the bound workspace).
 int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
                 const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
                 const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
-                void* stream, int32_t* backend_out) {
+                void* stream, int32_t* backend_out, bool use_static = false) {
   if (!ctx) return GKV_ERR_INVALID;
   const auto t_start = std::chrono::steady_clock::now();
   if (int r = read_topology(ctx)) return r;
@@ -522,7 +551,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   if (batch < 1) return fail(ctx, GKV_ERR_INVALID, "batch must be >= 1");
   if (!q || !out || !lse || !hot_prefix_ids || !cold_indptr_h)
     return fail(ctx, GKV_ERR_INVALID, "attn_decode: null pointer argument");
-  if (!ctx->ws) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
+  if (!use_static && !ctx->ws) return fail(ctx, GKV_ERR_INVALID, "no workspace bound");
   const gkv_config& c = ctx->cfg;
   const int32_t group = c.n_q_heads / c.n_kv_heads;
   const bool any_suffix = cold_indptr_h[batch] != cold_indptr_h[0];
@@ -555,20 +584,35 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   if (gkv::build_plan(shape, ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
     return fail(ctx, GKV_ERR_INVALID, err);
 
-  // workspace: [counters][status][prefix o][prefix lse][suffix o][suffix lse]
+  // workspace: [counters][status][prefix o][prefix lse][suffix o][suffix lse];
+  // static scratch: [status][counters (room for any context)][the same partials]
   const size_t row = static_cast<size_t>(c.head_dim) * partial_size(c);
-  const size_t off_po = control_bytes(c);
+  const size_t off_po = use_static ? gkv::kStaticControlBytes : control_bytes(c);
   const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
   const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
   const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
   const size_t need = off_sl + gkv::align256(plan.suffix_rows * 4);
-  if (need > ctx->ws_bytes)
+  if (use_static && need > gkv::kStaticScratchBytes)
+    return fail(ctx, GKV_ERR_INVALID, "step needs " + std::to_string(need) + " bytes of scratch; the static "
+                                      "scratch of gkv_decode_step_static holds " +
+                                          std::to_string(gkv::kStaticScratchBytes) +
+                                          " (use gkv_decode_step with a workspace)");
+  if (!use_static && need > ctx->ws_bytes)
     return fail(ctx, GKV_ERR_INVALID, "workspace too small: step needs " + std::to_string(need) +
                                           " bytes, " + std::to_string(ctx->ws_bytes) + " bound");
+  uint8_t* ws = static_cast<uint8_t*>(ctx->ws);
+  bool clear_static = false;
+  if (use_static) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_fail(ctx, "hipGetDevice", e);
+    if ((e = gkv::scratch_region(dev, &ws, &clear_static)) != hipSuccess)
+      return device_fail(ctx, "static scratch address (hipGetSymbolAddress)", e);
+    ctx->static_device = dev;
+  }
   const auto t_planned = std::chrono::steady_clock::now();
 
   const Layer& L = ctx->layers[layer];
-  uint8_t* ws = static_cast<uint8_t*>(ctx->ws);
   a.batch = batch;
   a.n_q = c.n_q_heads;
   a.n_kv = c.n_kv_heads;
@@ -588,8 +632,8 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   a.k_new = k_new;
   a.v_new = k_new ? v_new : nullptr;
   a.new_slots = k_new ? new_slots_d : nullptr;
-  a.counters = reinterpret_cast<int32_t*>(ws);
-  a.status = reinterpret_cast<int32_t*>(ws + counter_bytes(c));
+  a.counters = reinterpret_cast<int32_t*>(ws + (use_static ? gkv::kStaticCounterOffset : 0));
+  a.status = reinterpret_cast<int32_t*>(ws + (use_static ? 0 : counter_bytes(c)));
   a.spin_limit = ctx->spin_limit;
   a.partial_f32 = partial_size(c) == 4 ? 1 : 0;
   a.p_o = ws + off_po;
@@ -604,7 +648,13 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
     ev = &ctx->timing_events[2 * ctx->timing_used];
     ctx->timing_used++;
   }
-  if (ctx->ws_clear) {
+  if (use_static && clear_static) {
+    // first use of this device's scratch: status and every counter to zero
+    // (each step leaves the counters at zero again)
+    if ((e = gkv::launch_zero_i32(reinterpret_cast<int32_t*>(ws), gkv::kStaticControlBytes / 4, st)) != hipSuccess)
+      return device_fail(ctx, "scratch clear launch", e);
+  }
+  if (!use_static && ctx->ws_clear) {
     if ((e = gkv::launch_zero_i32(a.counters, control_bytes(c) / 4, st)) != hipSuccess)
       return device_fail(ctx, "counter clear launch", e);
     ctx->ws_clear = false;
@@ -651,6 +701,16 @@ int gkv_decode_step(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_ne
   if (!k_new) return fail(ctx, GKV_ERR_INVALID, "decode_step: null pointer argument");
   return decode_impl(ctx, layer, q, k_new, v_new, new_slots_d, batch, hot_prefix_ids, cold_indptr_h,
                      cold_indices_d, out, lse, stream, backend_out);
+}
+
+int gkv_decode_step_static(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* new_slots_d, int32_t batch, const int32_t* hot_prefix_ids,
+                           const int32_t* cold_indptr_h, const int32_t* cold_indices_d, void* out, float* lse,
+                           void* stream, int32_t* backend_out) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (!k_new) return fail(ctx, GKV_ERR_INVALID, "decode_step: null pointer argument");
+  return decode_impl(ctx, layer, q, k_new, v_new, new_slots_d, batch, hot_prefix_ids, cold_indptr_h,
+                     cold_indices_d, out, lse, stream, backend_out, true);
 }
 
 }  // extern "C"

@@ -32,6 +32,11 @@ hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStr
 hipError_t launch_stream_read(const void* p, size_t bytes, int32_t workgroups, uint32_t* sink,
                               hipStream_t stream);
 
+// Device address of the static scratch of the allocation-free step on
+// `device` (which must be current), from hipGetSymbolAddress on its first
+// use there; *first_use tells the caller to clear what must start at zero.
+hipError_t scratch_region(int device, uint8_t** ptr, bool* first_use);
+
 // Zeroes n int32 words at p (a fill kernel, so that it can be captured).
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream);
 

@@ -52,9 +52,17 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "kernels.h"
+
+// Scratch of the allocation-free step (gkv_decode_step_static): status word,
+// join counters and partial results in a static array of every device the
+// library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (it names a host-side stand-in): the device
+// address comes from hipGetSymbolAddress, once per device (scratch_region).
+static __device__ __align__(256) uint8_t scratch[gkv::kStaticScratchBytes];
 
 namespace gkv {
 namespace {
@@ -1567,6 +1575,26 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(int32_t* p, size_t n) {
 }
 
 }  // namespace
+
+hipError_t scratch_region(int device, uint8_t** ptr, bool* first_use) {
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  static bool used[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    // the caller made `device` current
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || reinterpret_cast<uintptr_t>(p) % 256 != 0) return hipErrorInvalidSymbol;
+    addr[device] = static_cast<uint8_t*>(p);
+  }
+  *ptr = addr[device];
+  *first_use = !used[device];
+  used[device] = true;
+  return hipSuccess;
+}
 
 hipError_t launch_zero_i32(int32_t* p, size_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;

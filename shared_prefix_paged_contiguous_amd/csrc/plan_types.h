@@ -159,4 +159,12 @@ constexpr int32_t kArgsTail = 0x47'4b'56'31;
 // (their outputs are not valid).  Zero while every step is well formed.
 constexpr int kDefaultSpinLimit = 1 << 16;
 
+// Static scratch of the allocation-free step, per device: a 256-byte status
+// line, the join counters of up to kMaxBatch requests x 256 KV heads, then
+// the step's partial results.
+constexpr size_t kStaticScratchBytes = size_t{32} << 20;
+constexpr size_t kStaticCounterOffset = 256;
+constexpr size_t kStaticControlBytes = kStaticCounterOffset + size_t{kMaxBatch} * 256 * 4;
+constexpr int kMaxDevices = 64;
+
 }  // namespace gkv

@@ -87,7 +87,7 @@ class DecodeState:
     def __init__(self, w: workloads.Workload, device: str = "cuda", n_layers: int = 1,
                  m_sat: int = 0, force_backend: int = binding.BACKEND_AUTO,
                  hot_capacity: Optional[int] = None, cold_capacity: Optional[int] = None,
-                 registry: bool = False, partial_dtype: str = "input"):
+                 registry: bool = False, partial_dtype: str = "input", bind_workspace: bool = True):
         s = w.spec
         self.w = w
         self.device = device
@@ -164,9 +164,11 @@ class DecodeState:
         self.indptr_d = torch.from_numpy(self.indptr_h).to(dev)
         self.indices_d = torch.from_numpy(self.indices_h).to(dev)
         self.q = w.q.to(dev)
-        ws_bytes = ctx.workspace_size(w.batch, int(self.indptr_h[-1]))
-        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        ctx.bind_workspace(self.workspace)
+        self.workspace = None
+        if bind_workspace:
+            ws_bytes = ctx.workspace_size(w.batch, int(self.indptr_h[-1]))
+            self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            ctx.bind_workspace(self.workspace)
         for layer in range(1, n_layers):
             self.add_layer_copy(layer)
 
