@@ -391,6 +391,90 @@ def run_bench(args):
     return res
 
 
+def timeline(args):
+    """Per-workgroup timeline of the step kernel (gkv_step_trace) on the
+    bench workload: each workgroup's start, mid-point mark and end from the
+    device's 100 MHz clock, over --tl-steps steps on rotating layer replicas.
+    Reports, per kind of workgroup (prefix split, suffix part or folded pair,
+    join), the percentiles of start, mark and end relative to the first start
+    of the step (microseconds), the kernel span, how many workgroups of each
+    kind are running in each 2 us bin (median step), and whether each prefix
+    workgroup ran on the XCD its index names (index modulo the XCD count)."""
+    import torch
+
+    from shared_prefix_paged_contiguous_amd import binding, workloads
+
+    w = workloads.make(args.workload)
+    force = {"auto": binding.BACKEND_AUTO, "cascade": binding.BACKEND_CASCADE,
+             "dense": binding.BACKEND_DENSE}[args.backend]
+    replicas = args.replicas or max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
+    st = build_state(w, replicas, force, args.partials)
+    k_new, v_new, slots = step_inputs(w, st)
+    out, lse = st.new_outputs()
+    for i in range(args.warmup):
+        st.step(out, lse, k_new, v_new, slots, layer=i % replicas)
+    torch.cuda.synchronize()
+    plan = st.ctx.last_plan()
+    grid = plan["n_prefix_blocks"] + plan["n_suffix_blocks"] + plan["n_join_blocks"]
+    buf = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+    st.ctx.step_trace(buf)
+    runs = []
+    for i in range(args.tl_steps):
+        buf.zero_()
+        st.step(out, lse, k_new, v_new, slots, layer=i % replicas)
+        torch.cuda.synchronize()
+        runs.append(buf.cpu().numpy().reshape(grid, 4).astype(np.int64))
+    st.ctx.step_trace(None)
+
+    n_kv = w.spec.n_kv
+    real_suffix = (((plan["n_suffix_parts"] + 1) // 2) if plan["folded_parts"] else plan["n_suffix_parts"]) * n_kv
+    xcds = None
+    stats = []
+    for rec in runs:
+        t0 = rec[:, 0].min()
+        us = lambda x: (x - t0) * 0.01   # 100 MHz ticks -> microseconds
+        kind = rec[:, 3] >> 32
+        xcc = (rec[:, 3] >> 16) & 0xF
+        xcds = int(xcc.max()) + 1
+        idx = np.arange(grid)
+        pre = (kind == 0) & (rec[:, 1] != 0)                     # prefix splits that ran (not XCD padding)
+        suf = (kind == 1) & (idx - plan["n_prefix_blocks"] < real_suffix)
+        joi = (kind == 2) & (rec[:, 1] != 0)                     # joins that waited (several partials)
+        row = {"span_us": float(us(rec[:, 2].max()))}
+        for name, m in (("prefix", pre), ("suffix", suf), ("join", joi)):
+            if not m.any():
+                continue
+            d = {"n": int(m.sum())}
+            for part, col in (("start", 0), ("mark", 1), ("end", 2)):
+                v = rec[m, col]
+                if part == "mark" and name == "suffix" and not plan["folded_parts"]:
+                    continue
+                x = us(v)
+                d[part] = [round(float(np.percentile(x, p)), 2) for p in (0, 50, 100)]
+            stats_m = us(rec[m, 2]) - us(rec[m, 0])
+            d["duration_p50"] = round(float(np.median(stats_m)), 2)
+            row[name] = d
+        row["prefix_on_named_xcd"] = float(np.mean(xcc[pre] == (idx[pre] % xcds))) if pre.any() else None
+        # running workgroups per kind in 2 us bins
+        edges = np.arange(0.0, row["span_us"] + 2.0, 2.0)
+        act = {}
+        for name, m in (("prefix", pre), ("suffix", suf), ("join", joi)):
+            s0, s1 = us(rec[m, 0]), us(rec[m, 2])
+            act[name] = [int(((s0 < e + 2.0) & (s1 > e)).sum()) for e in edges]
+        row["running_per_2us"] = act
+        stats.append(row)
+    order = np.argsort([r["span_us"] for r in stats])
+    med = stats[int(order[len(order) // 2])]
+    res = {"mode": "timeline", "workload": w.spec.name, "steps": len(stats), "xcds_seen": xcds,
+           "grid": {"prefix": plan["n_prefix_blocks"], "suffix": plan["n_suffix_blocks"],
+                    "join": plan["n_join_blocks"], "folded": plan["folded_parts"]},
+           "span_us_all": sorted(round(r["span_us"], 2) for r in stats), "median_step": med,
+           "note": "times in us from the step's first workgroup start (s_memrealtime, 100 MHz); "
+                   "[min, median, max] over workgroups; prefix mark = end of the block loop, "
+                   "suffix mark = end of the first part of a folded pair, join mark = end of the wait"}
+    print(json.dumps(res), flush=True)
+
+
 def fit_msat(args):
     """Re-fit the dispatcher threshold M_sat on this GPU.
 
@@ -633,6 +717,9 @@ def main():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (counter calibration)")
     ap.add_argument("--fit-msat", action="store_true")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timeline of the step kernel (gkv_step_trace), phase statistics")
+    ap.add_argument("--tl-steps", type=int, default=9)
     ap.add_argument("--paged-comparator", action="store_true",
                     help="time the prefix over a shared HOT slab vs per-request 16-token COLD pages")
     ap.add_argument("--cmp-batch", type=int, default=256)
@@ -660,6 +747,9 @@ def main():
         sys.exit(2)
     if args.fit_msat:
         fit_msat(args)
+        return
+    if args.timeline:
+        timeline(args)
         return
     if args.paged_comparator:
         paged_comparator(args)

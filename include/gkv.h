@@ -359,7 +359,8 @@ typedef struct {
                                  long one): chosen for cascade steps whose parts' workgroups
                                  overflow the workgroup slots beside the prefix while half as
                                  many fit */
-  int32_t reserved;
+  int32_t n_join_blocks;      /* join workgroups (one per request and KV head when some output
+                                 is joined from several partials, else 0) */
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
   double host_call_us;        /* host time of the whole call: validation, planning and the
@@ -383,6 +384,19 @@ int gkv_step_status(gkv_ctx* ctx, void* stream, int32_t* joins_timed_out);
  * default.  For tests of the give-up path (e.g. 0: a join that finds its
  * partials missing gives up at once, and the kernel still ends normally). */
 int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls);
+
+/* Measurement: per-workgroup timeline of the following step launches of this
+ * context.  With trace_dev non-null (dev, 8-byte aligned, `bytes` long) every
+ * step whose grid fits (32 bytes per workgroup; the grid is n_prefix_blocks +
+ * n_suffix_blocks + n_join_blocks of gkv_last_plan) writes, per workgroup b,
+ * four uint64 at trace_dev[4 b]: its start, a mid-point mark (prefix split:
+ * end of its block loop; suffix workgroup: end of its first part when it
+ * runs two, else 0; join: end of its wait), its end - s_memrealtime ticks
+ * of the 100 MHz clock common to the device - and (kind << 32) | (XCC id
+ * << 16) | (low 16 bits of the wave's HW_ID register), kind 0 = prefix,
+ * 1 = suffix, 2 = join.  A step whose grid does not fit is not traced.
+ * trace_dev NULL turns tracing off.  Host-only. */
+int gkv_step_trace(gkv_ctx* ctx, void* trace_dev, size_t bytes);
 
 /* Measurement: a plain streaming read of `bytes` (a multiple of 16) at dev
  * (16-byte aligned) by `workgroups` workgroups of 256 lanes, each lane keeping

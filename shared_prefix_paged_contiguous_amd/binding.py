@@ -58,7 +58,7 @@ class _PlanInfo(ctypes.Structure):
                 ("n_classes", ctypes.c_int32), ("n_prefix_blocks", ctypes.c_int32),
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
                 ("joins_partials", ctypes.c_int32), ("suffix_part_tokens", ctypes.c_int32),
-                ("folded_parts", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("folded_parts", ctypes.c_int32), ("n_join_blocks", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double),
                 ("host_call_us", ctypes.c_double)]
 
@@ -116,6 +116,7 @@ SIGNATURES = {
     "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
     "gkv_step_status": (ctypes.c_int, [_P, _P, _PI32]),
     "gkv_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
+    "gkv_step_trace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "gkv_set_join_spin_limit": (ctypes.c_int, [_P, _I32]),
     "gkv_kernel_timing": (ctypes.c_int, [_P, _I32]),
     "gkv_kernel_timing_read": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_float), _I32, _PI32]),
@@ -392,6 +393,13 @@ class Context:
         n = ctypes.c_int32()
         self._check(self._lib.gkv_step_status(self._h, _stream(stream), ctypes.byref(n)), "step_status")
         return n.value
+
+    def step_trace(self, trace_dev=None, nbytes: Optional[int] = None):
+        """gkv_step_trace: per-workgroup timeline records of the following
+        steps into trace_dev (a device tensor), or off with None."""
+        if trace_dev is not None and nbytes is None:
+            nbytes = trace_dev.numel() * trace_dev.element_size()
+        self._check(self._lib.gkv_step_trace(self._h, _ptr(trace_dev), nbytes or 0), "step_trace")
 
     def set_join_spin_limit(self, polls: int):
         self._check(self._lib.gkv_set_join_spin_limit(self._h, polls), "set_join_spin_limit")

@@ -62,6 +62,8 @@ struct gkv_ctx {
   gkv_plan_info last{};
   bool have_last = false;
   int32_t static_device = -1;   // device of the last allocation-free step (its scratch holds a status word)
+  uint64_t* trace = nullptr;    // per-workgroup timeline records (gkv_step_trace), null: off
+  size_t trace_bytes = 0;
 
   explicit gkv_ctx(const gkv_config& c)
       : cfg(c),
@@ -400,6 +402,15 @@ int gkv_stream_read(const void* dev, size_t bytes, int32_t workgroups, uint32_t*
   return GKV_OK;
 }
 
+int gkv_step_trace(gkv_ctx* ctx, void* trace_dev, size_t bytes) {
+  if (!ctx) return GKV_ERR_INVALID;
+  if (trace_dev && reinterpret_cast<uintptr_t>(trace_dev) % 8 != 0)
+    return fail(ctx, GKV_ERR_INVALID, "trace buffer must be 8-byte aligned");
+  ctx->trace = static_cast<uint64_t*>(trace_dev);
+  ctx->trace_bytes = trace_dev ? bytes : 0;
+  return GKV_OK;
+}
+
 int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls) {
   if (!ctx) return GKV_ERR_INVALID;
   if (polls < -1) return fail(ctx, GKV_ERR_INVALID, "spin limit must be >= 0 (or -1 for the default)");
@@ -641,6 +652,8 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   a.s_o = ws + off_so;
   a.s_lse = reinterpret_cast<float*>(ws + off_sl);
   a.narrow_ws = need < 0x7fffffffull ? 1 : 0;   // partial stores may use 32-bit offsets
+  const size_t grid = static_cast<size_t>(a.prefix_blocks) + a.suffix_blocks + a.join_blocks;
+  a.trace = ctx->trace && ctx->trace_bytes >= grid * gkv::kTraceWords * sizeof(uint64_t) ? ctx->trace : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   hipEvent_t* ev = nullptr;
@@ -671,7 +684,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   ctx->last.joins_partials = plan.multi_part;
   ctx->last.suffix_part_tokens = plan.part_tokens;
   ctx->last.folded_parts = plan.fold;
-  ctx->last.reserved = 0;
+  ctx->last.n_join_blocks = plan.join_blocks;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->last.host_call_us = std::chrono::duration<double, std::micro>(t_launched - t_start).count();

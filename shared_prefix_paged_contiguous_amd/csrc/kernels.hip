@@ -789,6 +789,23 @@ __device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, i
   __hip_atomic_fetch_add(cnt, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ timeline
+// Records of gkv_step_trace (see kTraceWords): one thread per workgroup
+// writes its start, a mark and its end.
+__device__ __forceinline__ void trace_start(const StepArgs& a, int blk, uint32_t kind) {
+  // HW_ID (hardware register 4) and XCC_ID (20), whole 32-bit fields
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xf;
+  uint64_t* r = a.trace + static_cast<size_t>(blk) * kTraceWords;
+  r[0] = __builtin_amdgcn_s_memrealtime();
+  r[1] = 0;
+  r[3] = (static_cast<uint64_t>(kind) << 32) | (xcc << 16) | (hw & 0xffff);
+}
+__device__ __forceinline__ void trace_mark(const StepArgs& a, int blk) {
+  if (a.trace && threadIdx.x == 0)
+    a.trace[static_cast<size_t>(blk) * kTraceWords + 1] = __builtin_amdgcn_s_memrealtime();
+}
+
 // ------------------------------------------------------------ suffix blocks
 // One (suffix part, KV head) per call; see StepArgs.  Each wave runs the
 // online softmax over its quarter of the part through the slot table and the
@@ -1053,6 +1070,7 @@ __device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t
   if (first > q) {
     suffix_part<T, D, P>(a, first, gk, smem_raw);
     __syncthreads();
+    trace_mark(a, a.prefix_blocks + blk);
   }
   suffix_part<T, D, P>(a, q, gk, smem_raw);
 }
@@ -1398,6 +1416,7 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
   // run across the lanes (the partial stores write through the caches, so
   // scattered pieces would cost partial-line writes).
   __syncthreads();   // every wave is done reading the ring
+  trace_mark(a, blk);
   constexpr int kStride = D + 4;   // padded row stride of the staging tile (floats)
   static_assert(kWaves * 16 * kStride * 4 <= kStages * 2 * kImg, "staging tile exceeds the ring");
   float* stage = reinterpret_cast<float*>(&ring[0][0]) + wave * 16 * kStride;
@@ -1484,6 +1503,7 @@ __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
   if (n == 1) return;   // finished by its only suffix part
   if (threadIdx.x == 0) wait_arrivals(a, b, g, n);
   __syncthreads();
+  trace_mark(a, a.prefix_blocks + a.suffix_blocks + j);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int col = wave; col < a.group; col += kWaves) join_row<T, D, P>(a, src, b, g * a.group + col, lane);
 }
@@ -1495,12 +1515,15 @@ void step_kernel(StepArgs a) {
   if (a.tail != kArgsTail) return;   // the work description did not arrive whole
   const int blk = blockIdx.x;
   const int work = a.prefix_blocks + a.suffix_blocks;
-  if (blk >= work) {
-    join_block<T, D, P>(a, blk - work);
-    return;
-  }
-  if (blk < a.prefix_blocks) prefix_block<T, D, RB, P>(a, blk, smem);
+  const uint32_t kind = blk >= work ? kTraceJoin : blk < a.prefix_blocks ? kTracePrefix : kTraceSuffix;
+  if (a.trace && threadIdx.x == 0) trace_start(a, blk, kind);
+  if (blk >= work) join_block<T, D, P>(a, blk - work);
+  else if (blk < a.prefix_blocks) prefix_block<T, D, RB, P>(a, blk, smem);
   else suffix_block<T, D, P>(a, blk - a.prefix_blocks, smem);
+  if (a.trace) {
+    __syncthreads();
+    if (threadIdx.x == 0) a.trace[static_cast<size_t>(blk) * kTraceWords + 2] = __builtin_amdgcn_s_memrealtime();
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, const u32x4* v_new,

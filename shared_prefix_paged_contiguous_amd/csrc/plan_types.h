@@ -141,7 +141,8 @@ struct StepArgs {
   void* s_o;                   // suffix-part partials, row = part * n_q + h (same dtype as p_o)
   float* s_lse;
   int32_t* counters;           // [kMaxBatch][n_kv] partial arrivals (zero between calls)
-  int32_t* status;             // status word: joins that gave up waiting (see kStatus*)
+  int32_t* status;             // status word: joins that gave up waiting (gkv_step_status)
+  uint64_t* trace;             // per-workgroup timeline records (kTraceWords each), null: off
   ClassDesc classes[kMaxClasses];
   alignas(16) RankDesc ranks[kMaxBatch];   // by rank
   // small-int tables, 4-byte aligned so entries can be read with 32-bit loads
@@ -158,6 +159,13 @@ constexpr int32_t kArgsTail = 0x47'4b'56'31;
 // number of joins that stopped waiting for their partials at the spin limit
 // (their outputs are not valid).  Zero while every step is well formed.
 constexpr int kDefaultSpinLimit = 1 << 16;
+
+// Timeline record of one workgroup (gkv_step_trace): start, a mid-point mark
+// (prefix: end of the block loop; suffix: end of the first part; join: end of
+// its wait), end - all s_memrealtime ticks (100 MHz) - and (kind << 32) | the
+// XCC id << 16 | the low 16 bits of HW_ID (wave, SIMD, CU, SH, SE).
+constexpr int kTraceWords = 4;
+enum TraceKind : uint32_t { kTracePrefix = 0, kTraceSuffix = 1, kTraceJoin = 2 };
 
 // Static scratch of the allocation-free step, per device: a 256-byte status
 // line, the join counters of up to kMaxBatch requests x 256 KV heads, then
