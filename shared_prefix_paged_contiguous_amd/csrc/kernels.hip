@@ -173,6 +173,10 @@ struct Traits<__bf16, D> {
       for (int j = 0; j < EPB; ++j) o.a[j][w] &= m;
     }
   }
+  // (The softmax denominators are summed on the VALU in fp32 from the
+  // unrounded weights: a sum of the bf16-rounded weights on the matrix cores,
+  // an all-ones block of this product, would cost up to 2^-9 of relative
+  // precision in lse.)
   __device__ static void pv(f32x4 (&acc)[EPB], const VOp& vo, const f32x4& p0, const f32x4& p1) {
     bf16x8 pb = {(__bf16)p0[0], (__bf16)p0[1], (__bf16)p0[2], (__bf16)p0[3],
                  (__bf16)p1[0], (__bf16)p1[1], (__bf16)p1[2], (__bf16)p1[3]};
@@ -271,6 +275,16 @@ struct ColState {
 #pragma unroll
     for (int j = 0; j < TR::EPB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // rescales the running state when the reference point moves by log2(alpha)
+  __device__ void rescale(float alpha) {
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < TR::EPB; ++j) acc[j] *= alpha;
+  }
+  // adds this block's weights (this lane's 8) to the running sum
+  __device__ void add_sum(const f32x4& p0, const f32x4& p1) {
+    l += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
+  }
 
   // One 32-token tile: K operands of the two 16-token halves, V operands, the
   // number of valid tokens (tokens >= valid are masked) and the score scale.
@@ -300,10 +314,7 @@ struct ColState {
                             fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) * c;
     if (__any(lmx > m + kLazy)) {
       const float m_new = fmaxf(m, wave_max_groups(lmx));
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < TR::EPB; ++j) acc[j] *= alpha;
+      rescale(__builtin_amdgcn_exp2f(m - m_new));
       m = m_new;
     }
     f32x4 p0, p1;
@@ -312,7 +323,7 @@ struct ColState {
       p0[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m));
       p1[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m));
     }
-    l += (p0[0] + p0[1]) + (p0[2] + p0[3]) + (p1[0] + p1[1]) + (p1[2] + p1[3]);
+    add_sum(p0, p1);
     TR::pv(acc, vo, p0, p1);
   }
 
@@ -364,10 +375,7 @@ __device__ __forceinline__ void tile_rows(ColState<T, D> (&st)[RB], const typena
                             fmaxf(fmaxf(s1[rb][0], s1[rb][1]), fmaxf(s1[rb][2], s1[rb][3]))) * c;
     if (__any(lmx > cs.m + kLazy)) {
       const float m_new = fmaxf(cs.m, wave_max_groups(lmx));
-      const float alpha = __builtin_amdgcn_exp2f(cs.m - m_new);
-      cs.l *= alpha;
-#pragma unroll
-      for (int j = 0; j < TR::EPB; ++j) cs.acc[j] *= alpha;
+      cs.rescale(__builtin_amdgcn_exp2f(cs.m - m_new));
       cs.m = m_new;
     }
 #pragma unroll
@@ -375,7 +383,7 @@ __device__ __forceinline__ void tile_rows(ColState<T, D> (&st)[RB], const typena
       p0[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[rb][i], c, -cs.m));
       p1[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[rb][i], c, -cs.m));
     }
-    cs.l += (p0[rb][0] + p0[rb][1]) + (p0[rb][2] + p0[rb][3]) + (p1[rb][0] + p1[rb][1]) + (p1[rb][2] + p1[rb][3]);
+    cs.add_sum(p0[rb], p1[rb]);
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
@@ -426,10 +434,7 @@ __device__ __forceinline__ void softmax_ref(ColState<T, D> (&st)[RB], f32x4 (&s0
     for (int rb = 0; rb < RB; ++rb) {
       ColState<T, D>& cs = st[rb];
       const float m_new = fmaxf(cs.m, wave_max_groups(lmx[rb]));
-      const float alpha = __builtin_amdgcn_exp2f(cs.m - m_new);
-      cs.l *= alpha;
-#pragma unroll
-      for (int j = 0; j < TR::EPB; ++j) cs.acc[j] *= alpha;
+      cs.rescale(__builtin_amdgcn_exp2f(cs.m - m_new));
       cs.m = m_new;
     }
   }
@@ -447,7 +452,7 @@ __device__ __forceinline__ void softmax_p(ColState<T, D> (&st)[RB], const f32x4 
       p0[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[rb][i], c, -cs.m));
       p1[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[rb][i], c, -cs.m));
     }
-    cs.l += (p0[rb][0] + p0[rb][1]) + (p0[rb][2] + p0[rb][3]) + (p1[rb][0] + p1[rb][1]) + (p1[rb][2] + p1[rb][3]);
+    cs.add_sum(p0[rb], p1[rb]);
   }
 }
 
@@ -1345,9 +1350,10 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
     // the matrix cores interleaved with the softmax of S(i) on the VALU, then
     // PV(i); last, the reference points for S(i + 1).  Only the last block
     // can be partial; it is masked when its scores are formed and done after
-    // the loop.
+    // the loop.  The loop is unrolled by two so that the score tiles of
+    // consecutive blocks alternate between two register sets (no copies).
     auto valid_of = [&](int j) { return min(kHotBlock, t1 - t0 - kHotBlock * j); };
-    f32x4 s0[RB], s1[RB];
+    f32x4 s0[RB], s1[RB], n0[RB], n1[RB];
     wait_block(0, min(nb - 1, kStages - 2));
     if (wave_active) {
       KOps k;
@@ -1355,7 +1361,8 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
       qk_rows<T, D, RB>(st, k.k0, k.k1, s0, s1);
       softmax_ref<T, D, RB>(st, s0, s1, valid_of(0), g, c);
     }
-    for (int i = 0; i + 1 < nb; ++i) {
+    // iteration i: S(i) in (c0, c1), S(i + 1) into (x0, x1)
+    auto iteration = [&](int i, f32x4 (&c0)[RB], f32x4 (&c1)[RB], f32x4 (&x0)[RB], f32x4 (&x1)[RB]) {
       wait_block(i + 1, min(nb - 1, i + kStages - 2));
       if (i + kStages - 1 < nb) copy(i + kStages - 1, (i + kStages - 1) % kStages);
       if (wave_active) {
@@ -1363,9 +1370,9 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
         KOps k;
         read_k(k, i + 1);
         read_v(vo, i);
-        f32x4 n0[RB], n1[RB], p0[RB], p1[RB];
-        qk_rows<T, D, RB>(st, k.k0, k.k1, n0, n1);
-        softmax_p<T, D, RB>(st, s0, s1, c, p0, p1);
+        f32x4 p0[RB], p1[RB];
+        qk_rows<T, D, RB>(st, k.k0, k.k1, x0, x1);
+        softmax_p<T, D, RB>(st, c0, c1, c, p0, p1);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
         // one MFMA of QK^T(i + 1), then VALU work of the softmax, repeated;
@@ -1375,12 +1382,20 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
-        softmax_ref<T, D, RB>(st, n0, n1, valid_of(i + 1), g, c);
+        softmax_ref<T, D, RB>(st, x0, x1, valid_of(i + 1), g, c);
+      }
+    };
+    int i = 0;
+    for (; i + 2 < nb; i += 2) {
+      iteration(i, s0, s1, n0, n1);
+      iteration(i + 1, n0, n1, s0, s1);
+    }
+    if (i + 1 < nb) {
+      iteration(i, s0, s1, n0, n1);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          s0[rb] = n0[rb];
-          s1[rb] = n1[rb];
-        }
+      for (int rb = 0; rb < RB; ++rb) {   // once per split: the last block's scores to (s0, s1)
+        s0[rb] = n0[rb];
+        s1[rb] = n1[rb];
       }
     }
     if (wave_active) {
