@@ -183,9 +183,10 @@ def build_state(w, replicas, force, partials="input"):
 def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
     """Measured read ceiling of this GPU, a second denominator beside the
     8 TB/s data-sheet peak: the library's plain streaming-read kernel
-    (gkv_stream_read: consecutive lanes read consecutive 16-byte vectors,
-    eight loads in flight per lane) over a 1 GiB buffer, at several grid
-    sizes, best of `reps` each; and, for context, a device copy (torch)."""
+    (gkv_stream_read: each wave reads 8 KB chunks with non-temporal loads,
+    eight 16-byte loads in flight per lane) over a 1 GiB buffer, at several
+    grid sizes, best of `reps` each; and, for context, a device copy
+    (torch)."""
     import torch
 
     from shared_prefix_paged_contiguous_amd import binding
@@ -209,7 +210,7 @@ def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
         return min(t)
 
     reads = {}
-    for wg in (512, 1024, 2048, 4096, 8192):
+    for wg in (256, 512, 1024, 2048, 4096):
         reads[wg] = n_bytes / best(lambda: binding.stream_read(x, n_bytes, wg, sink, stream)) / 1e9
     copy = 2 * n_bytes / best(lambda: y.copy_(x)) / 1e9
     del x, y
@@ -219,6 +220,20 @@ def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
             "read_gbps_by_workgroups": {str(k): round(v, 1) for k, v in reads.items()},
             "copy_gbps": round(copy, 1), "bytes": n_bytes,
             "how": "best of %d per grid size over a 1 GiB buffer; copy = torch copy_ (read + write)" % reps}
+
+
+def make_workload(args):
+    """The named workload, or a variant of it with another batch and/or
+    suffix-length range (--batch, --suffix-range LO,HI; e.g. prefix-only
+    steps at a large M_eff for counter runs of the dense backend)."""
+    from shared_prefix_paged_contiguous_amd import workloads
+    kw = {}
+    if args.batch:
+        kw["batch"] = args.batch
+    if args.suffix_range:
+        lo, hi = (int(x) for x in args.suffix_range.split(","))
+        kw["suffix_range"] = (lo, hi)
+    return workloads.make(args.workload, **kw)
 
 
 def step_inputs(w, st):
@@ -242,8 +257,9 @@ def run_bench(args):
     from shared_prefix_paged_contiguous_amd import binding, workloads
 
     t_setup = time.perf_counter()
-    w = workloads.make(args.workload)
+    w = make_workload(args)
     s = w.spec
+    derived = bool(args.batch or args.suffix_range)
     force = {"auto": binding.BACKEND_AUTO, "cascade": binding.BACKEND_CASCADE,
              "dense": binding.BACKEND_DENSE}[args.backend]
     replicas = args.replicas or max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
@@ -341,7 +357,8 @@ def run_bench(args):
     dom_bytes = alg["kernel_bytes"][dom]
     achieved = dom_bytes / (kern_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": counter_traffic(s.name),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if derived else counter_traffic(s.name),
                 "kernel": dom + "_kernel",
                 "kernel_us": round(kern_ms[dom] * 1e3, 2), "kernel_bytes": dom_bytes}
     if alg["prefix_flops"] > 0:
@@ -358,7 +375,8 @@ def run_bench(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": s.dtype,
         "data": "synthetic (seeded N(0,1), bf16-rounded; stands in for ShareGPT-V3)",
-        "config": {"workload": s.name, "description": s.description, "batch": w.batch,
+        "config": {"workload": s.name + (f" (batch {w.batch}, suffixes {args.suffix_range})" if derived else ""),
+                   "description": s.description, "batch": w.batch,
                    "n_q_heads": s.n_q, "n_kv_heads": s.n_kv, "head_dim": s.head_dim,
                    "prefix_tokens": alg["prefix_tokens"], "suffix_tokens": alg["suffix_tokens"],
                    "backend": binding.BACKEND_NAMES[backend], "m_eff": plan["m_eff"],
@@ -404,7 +422,7 @@ def timeline(args):
 
     from shared_prefix_paged_contiguous_amd import binding, workloads
 
-    w = workloads.make(args.workload)
+    w = make_workload(args)
     force = {"auto": binding.BACKEND_AUTO, "cascade": binding.BACKEND_CASCADE,
              "dense": binding.BACKEND_DENSE}[args.backend]
     replicas = args.replicas or max(2, math.ceil(MALL_DEFEAT_BYTES / estimate_step_bytes(w)))
@@ -543,7 +561,11 @@ def paged_comparator(args):
                 request's slot table: the prefix bytes are read B times.
     Times the step kernel of gkv_attn_decode on each (kernel start/end
     events; the HOT side rotates over 4 layer copies, more than the 256 MB
-    MALL holds) and checks that the two outputs agree."""
+    MALL holds) and checks that the two outputs agree.  Then the layout
+    alone, with the kernel held fixed: the same slot-table gather as
+    "paged" over one shared copy of the prefix in COLD (shared_pages:
+    16-token pages in random order; shared_slots: consecutive slots),
+    every request's table pointing at it."""
     import torch
 
     from shared_prefix_paged_contiguous_amd import binding, workloads
@@ -632,6 +654,51 @@ def paged_comparator(args):
     log(f"[cmp] paged: {us_pg:.1f} us, speedup of the HOT slab {us_pg / us_hot:.1f}x, "
         f"max |out diff| {err_o:.2e}, |lse diff| {err_l:.2e}")
     assert err_o <= 2e-2 and err_l <= 2e-2, res["max_abs_diff"]
+    del ws, ctx, k_cold, v_cold
+    torch.cuda.empty_cache()
+
+    # ---- the same slot-table gather over ONE copy of the prefix in COLD,
+    # referenced by every request's table: in 16-token pages in random order
+    # (shared_pages) and in consecutive slots (shared_slots).  Against
+    # "paged", only the layout changes (one shared copy instead of B), not
+    # the kernel; six layer copies rotate (6 x 64 MiB, beyond the MALL).
+    layers = 6
+    for name, shuffled in (("shared_pages", True), ("shared_slots", False)):
+        cap = plen + bsz
+        ctx = binding.Context(n_q, n_kv, d, "bf16", 0, cap, n_layers=layers)
+        if shuffled:
+            slots = (rng.permutation(plen // page)[:, None] * page + np.arange(page)[None, :]).reshape(-1)
+        else:
+            slots = np.arange(plen)
+        sl = torch.from_numpy(slots.astype(np.int32)).cuda()
+        own = torch.arange(plen, cap, dtype=torch.int32, device="cuda")
+        keep = []
+        for layer in range(layers):
+            k_cold = torch.zeros((cap, n_kv, d), dtype=torch.bfloat16, device="cuda")
+            v_cold = torch.zeros_like(k_cold)
+            ctx.bind_layer(layer, None, None, k_cold, v_cold)
+            ctx.cold_append(layer, pk, pv, sl)
+            ctx.cold_append(layer, ck, cv, own)
+            keep.append((k_cold, v_cold))
+        indices = np.concatenate([np.concatenate([slots, [plen + b]]) for b in range(bsz)]).astype(np.int32)
+        ws = torch.empty(ctx.workspace_size(bsz, int(indptr[-1])), dtype=torch.uint8, device="cuda")
+        ctx.bind_workspace(ws)
+        us_sh, out_sh, lse_sh = timed(ctx, layers, [-1] * bsz, indptr.astype(np.int32),
+                                      torch.from_numpy(indices).cuda())
+        e_o = float((out_sh.float().cpu() - out_hot).abs().max())
+        e_l = float((lse_sh.cpu() - lse_hot).abs().max())
+        res[name] = {"kernel_us": round(us_sh, 2), "prefix_bytes_in_pool": 2 * plen * row,
+                     "prefix_bytes_gathered": bsz * 2 * plen * row,
+                     "max_abs_diff_vs_hot": {"out": e_o, "lse": e_l}}
+        log(f"[cmp] {name}: {us_sh:.1f} us, max |out diff| {e_o:.2e}, |lse diff| {e_l:.2e}")
+        assert e_o <= 2e-2 and e_l <= 2e-2, res[name]
+        del keep, ws, ctx
+        torch.cuda.empty_cache()
+    # the layout effect with the kernel held fixed (the slot-table gather),
+    # and the effect of the HOT prefix tiles over the same shared copy
+    res["same_kernel_shared_slots_speedup"] = round(us_pg / res["shared_slots"]["kernel_us"], 2)
+    res["same_kernel_shared_pages_speedup"] = round(us_pg / res["shared_pages"]["kernel_us"], 2)
+    res["hot_tiles_vs_shared_slots"] = round(res["shared_slots"]["kernel_us"] / us_hot, 2)
     print(json.dumps(res), flush=True)
 
 
@@ -702,6 +769,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_lp16k_b64")
     ap.add_argument("--backend", default="auto", choices=["auto", "cascade", "dense"])
+    ap.add_argument("--batch", type=int, default=0,
+                    help="variant of the workload with this many requests (0: the workload's own)")
+    ap.add_argument("--suffix-range", default="",
+                    help="variant with suffix lengths U{LO..HI} tokens, as LO,HI (1,1: prefix-only steps)")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--partials", default="input", choices=["input", "f32"],
                     help="element type of the step's partial results (workspace) before their join: "
