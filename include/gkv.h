@@ -351,7 +351,7 @@ typedef struct {
   int32_t n_classes;          /* distinct HOT prefixes in the step */
   int32_t n_prefix_blocks;    /* prefix workgroups launched (incl. idle padding) */
   int32_t n_suffix_blocks;    /* suffix workgroups (parts x KV-head groups) */
-  int32_t n_suffix_parts;     /* slot-table parts (>= one per request) */
+  int32_t n_suffix_parts;     /* slot-table parts (>= one per request, short requests aside) */
   int32_t joins_partials;     /* 1 if some output is joined from several partials (a HOT
                                  prefix or a multi-part slot table), inside the step kernel */
   int32_t suffix_part_tokens; /* slot-table tokens per suffix part this step */
@@ -359,8 +359,13 @@ typedef struct {
                                  long one): chosen for cascade steps whose parts' workgroups
                                  overflow the workgroup slots beside the prefix while half as
                                  many fit */
-  int32_t n_join_blocks;      /* join workgroups (one per request and KV head when some output
-                                 is joined from several partials, else 0) */
+  int32_t n_join_blocks;      /* join workgroups (when some output is joined from several
+                                 partials: one per request and KV head, but one per short
+                                 request; else 0) */
+  int32_t n_short_requests;   /* short requests: a HOT prefix and at most 32 slot-table tokens.
+                                 They get no suffix part; one join workgroup per request
+                                 attends each KV head's slot-table tile itself and joins it
+                                 with the prefix splits */
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
   double host_call_us;        /* host time of the whole call: validation, planning and the
@@ -399,8 +404,9 @@ int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls);
 int gkv_step_trace(gkv_ctx* ctx, void* trace_dev, size_t bytes);
 
 /* Measurement: a plain streaming read of `bytes` (a multiple of 16) at dev
- * (16-byte aligned) by `workgroups` workgroups of 256 lanes, each lane keeping
- * eight 16-byte loads in flight; the data is discarded (sink_dev: 4 bytes of
+ * (16-byte aligned) by `workgroups` workgroups of 256 lanes: each wave reads
+ * 8 KB chunks with non-temporal loads (eight 16-byte loads in flight per
+ * lane), the waves striding over the buffer; the data is discarded (sink_dev: 4 bytes of
  * device memory that the kernel practically never writes).  Timed by the
  * caller on `stream`, it gives the device's achievable read bandwidth, the
  * ceiling the attention kernels are compared with beside the data-sheet

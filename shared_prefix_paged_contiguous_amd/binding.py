@@ -59,7 +59,7 @@ class _PlanInfo(ctypes.Structure):
                 ("n_suffix_blocks", ctypes.c_int32), ("n_suffix_parts", ctypes.c_int32),
                 ("joins_partials", ctypes.c_int32), ("suffix_part_tokens", ctypes.c_int32),
                 ("folded_parts", ctypes.c_int32), ("n_join_blocks", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double),
+                ("n_short_requests", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64), ("host_plan_us", ctypes.c_double),
                 ("host_call_us", ctypes.c_double)]
 
 

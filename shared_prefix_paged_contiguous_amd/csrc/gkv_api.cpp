@@ -685,6 +685,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   ctx->last.suffix_part_tokens = plan.part_tokens;
   ctx->last.folded_parts = plan.fold;
   ctx->last.n_join_blocks = plan.join_blocks;
+  ctx->last.n_short_requests = plan.n_short;
   ctx->last.workspace_bytes = static_cast<int64_t>(need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->last.host_call_us = std::chrono::duration<double, std::micro>(t_launched - t_start).count();

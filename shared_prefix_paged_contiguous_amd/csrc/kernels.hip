@@ -409,7 +409,6 @@ __device__ __forceinline__ void qk_rows(const ColState<T, D> (&st)[RB], const ty
 template <typename T, int D, int RB>
 __device__ __forceinline__ void softmax_ref(ColState<T, D> (&st)[RB], f32x4 (&s0)[RB], f32x4 (&s1)[RB], int valid, int g,
                                             float c) {
-  using TR = Traits<T, D>;
   if (valid < 32) {
     int v = __builtin_amdgcn_readfirstlane(valid);
     asm volatile("" : "+s"(v));
@@ -754,6 +753,73 @@ __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, 
   }
   if (lane == 0)
     a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
+}
+
+// Joins the partials of request b for the G query heads of KV head gk, 64 /
+// CH heads per pass: lane l takes 16-byte chunk l % CH of query head
+// gk * G + l / CH and walks the partials itself, NB at a time with all their
+// lse and chunk loads issued together, against a running reference point.
+// One round trip per NB partials for a whole KV head (short requests have
+// few partials per head: their prefix splits and their tile).
+template <typename T, int D, typename P>
+__device__ __forceinline__ void join_group(const StepArgs& a, const JoinSrc& src, int b, int gk, int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
+  constexpr int HP = 64 / CH;                                  // query heads per pass
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));      // values per chunk
+  constexpr int NB = 32;                                       // partials per batch
+  static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
+  const int ns = src.ns, np = ns + src.n_parts, G = a.group;
+  const int ch = lane % CH;
+  for (int h0 = 0; h0 < G; h0 += HP) {
+    const int col = h0 + lane / CH;
+    const int h = gk * G + min(col, G - 1);
+    const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
+    auto row_of = [&](int p) -> size_t {
+      return p < ns ? prow0 + static_cast<size_t>(p) * a.n_q : static_cast<size_t>(src.c0 + p - ns) * a.n_q + h;
+    };
+    float m = kNegInf, wsum = 0.f;
+    float acc[EPC];
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+    for (int base = 0; base < np; base += NB) {
+      float lp[NB];
+      u32x4 raw[NB];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {   // indices past the last partial repeat it and weigh zero
+        const int p = min(base + k, np - 1);
+        lp[k] = base + k < np ? load_partial((p < ns ? a.p_lse : a.s_lse) + row_of(p)) : kNegInf;
+        raw[k] = load_partial_chunk(static_cast<const P*>(p < ns ? a.p_o : a.s_o) + row_of(p) * D + EPC * ch);
+      }
+      float mb = m;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) mb = fmaxf(mb, lp[k]);
+      if (mb == kNegInf) continue;   // no tokens in any partial so far
+      const float sc = __builtin_amdgcn_exp2f(m - mb);   // 0 while m is -inf
+      wsum *= sc;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] *= sc;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float wk = lp[k] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(lp[k] - mb);
+        wsum += wk;
+        float v[EPC];
+        unpack_chunk<P>(raw[k], v);
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) acc[j] += wk * v[j];
+      }
+      m = mb;
+    }
+    // no tokens in any partial: an empty result, o = 0 and lse = -inf
+    const bool empty = !(wsum > 0.f);
+    const float inv = empty ? 0.f : 1.f / wsum;
+    if (col < G) {
+      T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + EPC * ch;
+#pragma unroll
+      for (int k = 0; k < EPC; ++k) dst[k] = static_cast<T>(acc[k] * inv);
+      if (ch == 0)
+        a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (m + __log2f(wsum)) * 0.69314718055994531f;
+    }
+  }
 }
 
 // Counts the arrival of one partial of (request b, KV head g).  Protocol:
@@ -1375,12 +1441,15 @@ __device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t
         softmax_p<T, D, RB>(st, c0, c1, c, p0, p1);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
-        // one MFMA of QK^T(i + 1), then VALU work of the softmax, repeated;
-        // the PV products follow
+        // 16 VALU instructions of the softmax first (the first QK^T(i + 1)
+        // product waits for K(i + 1) from LDS, and issue is in order: work
+        // placed behind it would wait too), then one MFMA of QK^T(i + 1) and
+        // two VALU instructions, repeated; the PV products follow
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
 #pragma unroll
         for (int x = 0; x < 2 * RB * TR::KS; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
         softmax_ref<T, D, RB>(st, x0, x1, valid_of(i + 1), g, c);
       }
@@ -1506,26 +1575,125 @@ constexpr size_t step_smem_bytes() {
   return sizeof(PrefixSmem<T, D>) > sizeof(SuffixSmem<T, D>) ? sizeof(PrefixSmem<T, D>) : sizeof(SuffixSmem<T, D>);
 }
 
-// Join of (request b, KV head g): waits for the arrival of all partials,
-// then wave w joins the request's query heads g*G + w, g*G + w + 4, ...
-// Where the partials lie is read before the wait, so after it only the
-// partials themselves are loaded.
+// Join of a short request (rank r >= inline_rank0: a HOT prefix and at most
+// kInlineTokens slot-table tokens, no suffix part), in three phases.
+// Tiles: wave w takes KV heads w, w + 4, ... and attends the request's
+// slot-table tile for each (one 32-token tile through the slot ids; in a
+// fused step the last entry is the new token, read from its input row and
+// copied into its slot, as a suffix part does), writing the normalised rows
+// and lse to the request's own partial rows (part0).  Wait: once these
+// stores are complete, one thread per KV head waits for the head's prefix
+// splits.  Join: wave w joins KV heads w, w + 4, ... (join_group).  The
+// tiles need no prefix result, so with free slots they run beside it.
+template <typename T, int D, typename P>
+__device__ __forceinline__ void short_join(const StepArgs& a, int r, int blk) {
+  using TR = Traits<T, D>;
+  using KOp = typename TR::KOp;
+  using VVec = typename TR::VVec;
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));   // values per 16-byte chunk of a partial row
+  const RankDesc rd = a.ranks[r];
+  const int b = rd.req, len = rd.tok1 - rd.tok0;
+  const JoinSrc src = {a.classes[table_at(a.req_class, b)].n_splits, rd.part0, 1};
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int G = a.group;
+  const bool col_ok = n < G;
+  const float c = a.scale_log2;
+  const size_t stride = static_cast<size_t>(a.n_kv) * D;
+  const bool fresh = a.k_new != nullptr && len > 0;
+  // the tile's slot ids, one per lane, clamped into the pool; the new token
+  // of a fused step: -1
+  int id = 0;
+  if (lane < len) id = min(max(a.cold_indices[rd.tok0 + lane], 0), a.cold_cap - 1);
+  if (fresh && lane == len - 1) id = -1;
+  for (int gk = wave; gk < a.n_kv; gk += kWaves) {
+    if (fresh) suffix_copy_new<T, D>(a, b, gk, lane);
+    float lse2 = kNegInf;
+    float o[D / 4];
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) o[k] = 0.f;
+    const int h = gk * G + (col_ok ? n : 0);
+    if (len > 0) {
+      ColState<T, D> st;
+      st.init();
+      if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
+      else TR::zero_row(st.q);
+      const T* kc = static_cast<const T*>(a.k_cold) + gk * D;
+      const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
+      const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
+      const T* knew = static_cast<const T*>(a.k_new) + new_row;
+      const T* vnew = static_cast<const T*>(a.v_new) + new_row + TR::EPB * n;
+      // row of tile position i (positions past the table repeat its last
+      // entry; the tile masks them)
+      auto row = [&](const T* pool, const T* fresh_row, int i) {
+        const int t = __shfl(id, min(i, len - 1));
+        return t < 0 ? fresh_row : pool + static_cast<size_t>(t) * stride;
+      };
+      KOp k0[TR::KS], k1[TR::KS];
+      VVec v[8];
+      TR::load_row(k0, row(kc, knew, n), g);
+      TR::load_row(k1, row(kc, knew, 16 + n), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = TR::load_v(row(vc, vnew, tau(g, e)));
+      typename TR::VOp vo;
+      TR::make_vop(vo, v);
+      st.tile(k0, k1, vo, len, g, c);
+      lse2 = st.finish(o);
+    }
+    // lane (n, g) holds d = (D/4) g .. of query head h: whole 16-byte chunks
+    if (col_ok) {
+      const size_t row = static_cast<size_t>(rd.part0) * a.n_q + h;
+      P* dst = static_cast<P*>(a.s_o) + row * D + (D / 4) * g;
+#pragma unroll
+      for (int k = 0; k < D / 4; k += EPC) {
+        float x[EPC];
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) x[j] = o[k + j];
+        store_chunk(dst + k, pack_chunk<P>(x), false);
+      }
+      if (g == 0) store_partial(a.s_lse + row, lse2);
+    }
+  }
+  wait_stores();
+  __syncthreads();
+  for (int gk = threadIdx.x; gk < a.n_kv; gk += kThreads) wait_arrivals(a, b, gk, src.ns);
+  __syncthreads();
+  trace_mark(a, blk);
+  for (int gk = wave; gk < a.n_kv; gk += kWaves) join_group<T, D, P>(a, src, b, gk, lane);
+}
+
+// Join j: for j < inline_rank0 * n_kv, (ranked request, KV head g) with the
+// ranks taken shortest slot table first (their partials arrive first): waits
+// for the arrival of all partials, then wave w joins the request's query
+// heads g*G + w, g*G + w + 4, ...  Where the partials lie is read before the
+// wait, so after it only the partials themselves are loaded.  The rest: one
+// short request each.
 template <typename T, int D, typename P>
 __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
-  const int b = j / a.n_kv, g = j - (j / a.n_kv) * a.n_kv;
+  const int blk = a.prefix_blocks + a.suffix_blocks + j;
+  const int nj = a.inline_rank0 * a.n_kv;
+  if (j >= nj) {
+    short_join<T, D, P>(a, a.inline_rank0 + (j - nj), blk);
+    return;
+  }
+  const int q = j / a.n_kv, g = j - q * a.n_kv;
+  const int b = a.ranks[a.inline_rank0 - 1 - q].req;
   const JoinSrc src = join_src(a, b);
   const int n = src.ns + src.n_parts;
   if (n == 1) return;   // finished by its only suffix part
   if (threadIdx.x == 0) wait_arrivals(a, b, g, n);
   __syncthreads();
-  trace_mark(a, a.prefix_blocks + a.suffix_blocks + j);
+  trace_mark(a, blk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int col = wave; col < a.group; col += kWaves) join_row<T, D, P>(a, src, b, g * a.group + col, lane);
 }
 
+// Two workgroups per CU; fp32 rows of 128 take 96 KB of LDS per prefix
+// workgroup, so one.
 template <typename T, int D, int RB, typename P>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void step_kernel(StepArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && D == 128 ? 1 : 2))) void step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
   if (a.tail != kArgsTail) return;   // the work description did not arrive whole
   const int blk = blockIdx.x;
@@ -1585,21 +1753,30 @@ hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, 
 }
 
 // Streaming read of n16 16-byte vectors (the measured read ceiling of the
-// device): consecutive lanes read consecutive vectors, eight loads in flight
-// per lane, and the data only feeds an xor whose (practically never taken)
-// store to `sink` keeps the loads alive.
+// device).  Each wave reads 8 KB chunks (eight 1 KB loads, consecutive lanes
+// on consecutive vectors, all in flight at once) with non-temporal loads,
+// the waves striding over the chunks; the fastest plain read pattern found on
+// gfx950 (grid-stride loads of single vectors reach about 12% less).  The
+// data only feeds an xor whose (practically never taken) store to `sink`
+// keeps the loads alive.
 __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* p, int64_t n16, uint32_t* sink) {
+  constexpr int kChunk = 8 * 64;   // vectors per wave chunk
   uint32_t acc = 0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t full = n16 / kChunk;
+  for (int64_t c = wave; c < full; c += waves) {
+    const u32x4* q = p + c * kChunk + lane;
     u32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = p[i + k * stride];
+    for (int k = 0; k < 8; ++k) v[k] = __builtin_nontemporal_load(q + 64 * k);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
   }
-  for (; i < n16; i += stride) {
+  // the last partial chunk, one vector per lane of the grid
+  for (int64_t i = full * kChunk + static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const u32x4 v = p[i];
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }

@@ -165,7 +165,8 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   if (backend == GKV_BACKEND_CASCADE && n_classes > 0) {
     int64_t parts = 0;
     for (int32_t b = 0; b < batch; ++b)
-      parts += std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
+      if (indptr[b + 1] - indptr[b] > kInlineTokens || a.req_class[b] < 0)   // short requests have none
+        parts += std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
     const int64_t pairs = ceil_div(parts, 2) * n_kv;
     if (parts > 1 && parts * n_kv > step_slots - blocks && pairs > step_slots - blocks &&
         pairs <= step_slots - pad) {
@@ -182,18 +183,30 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   plan.prefix_rows = static_cast<int64_t>(batch) * max_splits * n_q;
 
   // ---- suffix parts, longest slot table first (so the longest workgroups
-  // start first and the kernel's tail is short)
+  // start first and the kernel's tail is short); short requests (a HOT
+  // prefix and at most kInlineTokens slot-table tokens) last, without parts:
+  // their join workgroups attend their tables
+  auto is_short = [&](int32_t b) {
+    return a.req_class[b] >= 0 && indptr[b + 1] - indptr[b] <= kInlineTokens;
+  };
   int32_t order[kMaxBatch];
   for (int32_t b = 0; b < batch; ++b) order[b] = b;
   std::stable_sort(order, order + batch, [&](int32_t x, int32_t y) {
+    const bool sx = is_short(x), sy = is_short(y);
+    if (sx != sy) return sy;
     return indptr[x + 1] - indptr[x] > indptr[y + 1] - indptr[y];
   });
   int64_t parts = 0;
   int32_t multi = 0;
+  int32_t inline_rank0 = batch;
   for (int32_t r = 0; r < batch; ++r) {
     const int32_t b = order[r];
     a.rank_of[b] = static_cast<int16_t>(r);
     a.ranks[r] = RankDesc{indptr[b], indptr[b + 1], static_cast<int32_t>(parts), b};
+    if (is_short(b)) {
+      inline_rank0 = std::min(inline_rank0, r);
+      continue;
+    }
     const int64_t np = std::max<int64_t>(1, ceil_div(indptr[b + 1] - indptr[b], kSuffixPart));
     if (np > 1) multi = 1;
     parts += np;
@@ -217,13 +230,18 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   plan.fold = a.fold;
   a.multi_part = multi;
   a.need_merge = multi || n_classes > 0;
-  a.join_blocks = a.need_merge ? batch * n_kv : 0;
+  a.inline_rank0 = inline_rank0;
+  // each short request's tiles go to a partial row set of its own, after
+  // the suffix parts' rows
+  for (int32_t r = inline_rank0; r < batch; ++r) a.ranks[r].part0 = static_cast<int32_t>(parts) + (r - inline_rank0);
+  a.join_blocks = a.need_merge ? inline_rank0 * n_kv + (batch - inline_rank0) : 0;
+  plan.n_short = batch - inline_rank0;
   plan.n_parts = static_cast<int32_t>(parts);
   plan.part_tokens = kSuffixPart;
   plan.suffix_blocks = a.suffix_blocks;
   plan.join_blocks = a.join_blocks;
   plan.multi_part = a.need_merge;
-  plan.suffix_rows = a.need_merge ? parts * n_q : 0;
+  plan.suffix_rows = a.need_merge ? (parts + (batch - inline_rank0)) * n_q : 0;
   return 0;
 }
 

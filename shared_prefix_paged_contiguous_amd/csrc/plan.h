@@ -31,13 +31,14 @@ struct Plan {
   int32_t prefix_blocks = 0;    // prefix workgroups (including idle XCD padding)
   int32_t suffix_blocks = 0;    // suffix workgroups (incl. padding)
   int32_t join_blocks = 0;      // join workgroups
-  int32_t n_parts = 0;          // suffix parts (>= one per request)
+  int32_t n_parts = 0;          // suffix parts (>= one per request but the short ones)
   int32_t multi_part = 0;       // some request's output is joined from several partials
   int64_t prefix_rows = 0;      // prefix partial rows (B * max_splits * n_q)
   int64_t suffix_rows = 0;      // suffix partial rows
   int32_t part_tokens = 0;      // slot-table tokens per suffix part
   int32_t rb = 1;               // row blocks per wave of the prefix tiles
   int32_t fold = 0;             // suffix workgroups run folded pairs of parts
+  int32_t n_short = 0;          // short requests, attended by their own join workgroups
 };
 
 // Rule alone: dense iff batch * group >= m_sat (unless forced).

@@ -69,16 +69,18 @@ struct ClassDesc {
 };
 
 // Suffix work: one workgroup per (suffix part, KV head).  Requests are
-// ranked longest slot table first; rank r owns parts [ranks[r].part0,
+// ranked longest slot table first (short requests last, see below); rank r
+// owns parts [ranks[r].part0,
 // ranks[r].part0 + n) with n = max(1, ceil(table length / kSuffixPart))
-// (at least one, so every request gets a merge epilogue); part j covers its table positions [j * kSuffixPart, (j+1) * kSuffixPart)
-// and the 4 waves take consecutive quarters of it.  Block i -> part
-// i / n_kv, KV head i % n_kv.  A request with no HOT prefix and one part is
-// finished in the suffix workgroup's epilogue.  Otherwise every prefix split
-// and suffix part writes a partial per (request, query head) and counts its
-// arrival on the (request, KV head) counter; a join workgroup per (request,
-// KV head), placed after all prefix and suffix work in the grid, waits for
-// the count and joins the partials into the output.
+// (at least one, so every request gets a merge epilogue); part j covers its
+// table positions [j * kSuffixPart, (j+1) * kSuffixPart) and the 4 waves
+// take consecutive quarters of it.  Block i -> part i / n_kv, KV head
+// i % n_kv.  A request with no HOT prefix and one part is finished in the
+// suffix workgroup's epilogue.  Otherwise every prefix split and suffix part
+// writes a partial per (request, query head) and counts its arrival on the
+// (request, KV head) counter; a join workgroup, placed after all prefix and
+// suffix work in the grid, waits for the count and joins the partials into
+// the output.
 //
 // Folding (cascade steps): when the parts' workgroups would not all fit in
 // the workgroup slots the prefix leaves but half as many would, suffix block
@@ -89,16 +91,29 @@ struct ClassDesc {
 // running after the prefix ends; and each workgroup finishes on a long part,
 // which keeps many loads in flight to the end.
 //
-// Grid: prefix blocks, then suffix blocks, then batch * n_kv join blocks.
-// Prefix and suffix blocks never wait, and every join block follows all of
-// them in each XCD's (in-order) dispatch, so the joins' waits end.
-// The prefix and suffix ranges of the grid are padded to 4 * xcds blocks.
+// Short requests: a request with a HOT prefix whose slot table holds at
+// most kInlineTokens tokens (one tile) gets no suffix part.  Ranked after all
+// other requests, it has one join workgroup of its own that attends every KV
+// head's slot-table tile itself (wave w takes KV heads w, w + 4, ...) into a
+// partial row set of its own (rows after the suffix parts'; ranks[r].part0
+// names it), waits once for the prefix splits of all its KV heads and joins
+// them.  Steps whose requests carry a token or a few each (prefix-bound
+// steps) thus launch one workgroup per request, instead of two per
+// (request, KV head), and its tiles overlap the prefix when slots are free.
+constexpr int kInlineTokens = 32;
+//
+// Grid: prefix blocks, then suffix blocks, then the joins: one per (ranked
+// request, KV head) for the requests ranked before inline_rank0, shortest
+// slot table first, then one per short request.  Prefix and suffix blocks
+// never wait, and every join block follows all of them in each XCD's
+// (in-order) dispatch, so the joins' waits end.  The prefix and suffix
+// ranges of the grid are padded to 4 * xcds blocks.
 constexpr int kGroupPerXcd = 4;
 
 // A ranked request's suffix work in one 16-byte record (one scalar load).
 struct RankDesc {
   int32_t tok0, tok1;   // its slot-table range [tok0, tok1) in cold_indices
-  int32_t part0;        // its first suffix part
+  int32_t part0;        // its first suffix part (short requests: its tile rows, >= n_parts)
   int32_t req;          // the request (batch index)
 };
 
@@ -119,6 +134,8 @@ struct StepArgs {
   int32_t narrow_ws;           // the step's workspace spans less than 2 GB (32-bit store offsets)
   int32_t fold;                // suffix block i runs parts n_parts-1-i/n_kv and i/n_kv (see above)
   int32_t partial_f32;         // partial rows are fp32 (else the input dtype)
+  int32_t inline_rank0;        // ranks [inline_rank0, batch) are short requests (no suffix part)
+  int32_t pad1_;
   const void* q;
   void* out;
   float* lse;

@@ -231,6 +231,47 @@ def test_mixed_prefix_and_suffix_only_requests():
     check(out, lse, *oracle_ref(w))
 
 
+# ------------------------------------------------------- short requests
+@pytest.mark.parametrize("n_q,n_kv,d,dtype,force",
+                         [(n_q, n_kv, d, "bf16", f) for n_q, n_kv, d in ((32, 8, 128), (20, 4, 64), (16, 2, 128),
+                                                                         (8, 8, 64)) for f in (CASCADE, DENSE)]
+                         + [(32, 8, 64, "f32", AUTO), (8, 2, 128, "f32", AUTO)])   # fp32: cascade only
+def test_short_requests_join_their_own_tiles(n_q, n_kv, d, dtype, force):
+    """Requests with a HOT prefix and at most 32 slot-table tokens (0, 1, 2,
+    17, 31 and 32 here; 33 is not short) get no suffix part: one join
+    workgroup per request attends each KV head's tile (waves take KV heads
+    w, w + 4, ...; fewer than four KV heads leave waves idle; G from 1 to 5)
+    and joins it with the prefix splits."""
+    lens = (0, 1, 2, 17, 31, 32, 33, 1)
+    s = spec(n_q=n_q, n_kv=n_kv, head_dim=d, dtype=dtype, batch=len(lens), prefix_len=700, fixed_suffix=lens)
+    w = workloads.make(s)
+    st, out, lse, _ = run(w, force=force)
+    plan = st.ctx.last_plan()
+    assert plan["n_short_requests"] == 7 and plan["n_suffix_parts"] == 1
+    assert plan["n_join_blocks"] == n_kv + 7
+    check(out, lse, *oracle_ref(w), **(FP32_TOL if dtype == "f32" else {}))
+
+
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_prefix_bound_step_of_short_requests(force):
+    """A prefix-bound step: 256 requests of the Llama-3.1-8B attention shape
+    on one 2K prefix, each with its current token only: no suffix workgroup,
+    one join workgroup per request, and every request matches the oracle on
+    two calls in a row (the join counters return to zero)."""
+    s = spec(batch=256, prefix_len=2048, hot_capacity=2048, cold_capacity=512, fixed_suffix=(1,) * 256)
+    w = workloads.make(s)
+    st, out, lse, _ = run(w, force=force)
+    plan = st.ctx.last_plan()
+    assert plan["n_suffix_blocks"] == 0 and plan["n_short_requests"] == 256 and plan["n_join_blocks"] == 256
+    ref = oracle_ref(w)
+    check(out, lse, *ref)
+    out, lse = st.new_outputs()
+    st.run(out, lse)
+    torch.cuda.synchronize()
+    check(out, lse, *ref)
+    assert st.ctx.step_status() == 0
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_heterogeneous_classes(force):
     s = dataclasses.replace(workloads.SPECS["hetero8"], n_prefixes=3, prefix_len_lo=100, prefix_len_hi=1100,
@@ -328,15 +369,23 @@ def test_long_suffixes_span_several_parts(force):
     pt = plan["suffix_part_tokens"]
     assert pt % 32 == 0 and 64 <= pt <= 4096
     assert plan["joins_partials"] == 1
-    assert plan["n_suffix_parts"] == sum(max(1, -(-n // pt)) for n in (5000, 10, 0, 9000))
+    # the 10- and 0-token tables are short requests (joined with their tiles, no part)
+    assert plan["n_short_requests"] == 2
+    assert plan["n_suffix_parts"] == sum(max(1, -(-n // pt)) for n in (5000, 9000))
     check(out, lse, *oracle_ref(w))
 
 
 def _fold_lengths(batch):
-    # short tables, one prefix-only request and one two-part table
-    lens = np.random.default_rng(batch).integers(1, 200, batch)
-    lens[3], lens[7] = 0, 5000
+    # tables of 33..199 tokens, one prefix-only request, two more short
+    # requests (1 and 32 tokens) and one two-part table
+    lens = np.random.default_rng(batch).integers(33, 200, batch)
+    lens[3], lens[7], lens[11], lens[12] = 0, 5000, 1, 32
     return tuple(int(x) for x in lens)
+
+
+def _parts(lens, short=32, part=4096):
+    """Suffix parts of a step whose requests all have a HOT prefix."""
+    return sum(max(1, -(-n // part)) for n in lens if n > short)
 
 
 @pytest.mark.parametrize("batch,dtype", [(64, "bf16"), (65, "bf16"), (65, "f32")])
@@ -350,8 +399,10 @@ def test_folded_suffix_parts_parity(batch, dtype):
     w = workloads.make(s)
     st, out, lse, backend = run(w, force=CASCADE)
     plan = st.ctx.last_plan()
-    assert plan["folded_parts"] == 1 and plan["n_suffix_parts"] == batch + 1
-    assert plan["n_suffix_blocks"] == -(-(-(-(batch + 1) // 2) * 8) // 32) * 32
+    parts = _parts(_fold_lengths(batch))
+    assert parts == batch - 2 and plan["n_short_requests"] == 3
+    assert plan["folded_parts"] == 1 and plan["n_suffix_parts"] == parts
+    assert plan["n_suffix_blocks"] == -(-(-(-parts // 2) * 8) // 32) * 32
     tol = FP32_TOL if dtype == "f32" else {}
     ref = oracle_ref(w)
     check(out, lse, *ref, **tol)
@@ -368,14 +419,14 @@ def test_fold_rule():
     """No folding when the parts fit beside the prefix, when even half as
     many would not, for suffix-only steps whose parts fill the slots exactly,
     or under the dense backend."""
-    few = workloads.make(spec(n_kv=8, batch=40, prefix_len=256, hot_capacity=256, fixed_suffix=(9,) * 40))
+    few = workloads.make(spec(n_kv=8, batch=40, prefix_len=256, hot_capacity=256, fixed_suffix=(40,) * 40))
     st, *_ = run(few, force=CASCADE)
     assert st.ctx.last_plan()["folded_parts"] == 0
     only = workloads.make(spec(n_kv=8, batch=64, prefix_len=0, hot_capacity=0, fixed_suffix=(9,) * 64))
     st, *_ = run(only, force=CASCADE)
     assert st.ctx.last_plan()["folded_parts"] == 0 and st.ctx.last_plan()["n_suffix_blocks"] == 512
     many = workloads.make(spec(n_q=32, n_kv=8, head_dim=64, batch=128, prefix_len=256, hot_capacity=256,
-                               cold_capacity=4096, fixed_suffix=(9,) * 128))
+                               cold_capacity=8192, fixed_suffix=(40,) * 128))
     for force in (CASCADE, DENSE):              # 1024 part workgroups, 480 free slots
         st, out, lse, _ = run(many, force=force)
         assert st.ctx.last_plan()["folded_parts"] == 0
@@ -412,6 +463,7 @@ def _fused_cases():
         "fallback_to_cold": (spec(batch=4, prefix_len=900, fixed_suffix=(3, 50, 129, 400)), AUTO, "cold"),
         "multi_part": (spec(batch=4, prefix_len=300, hot_capacity=512, cold_capacity=20000,
                             fixed_suffix=(5000, 10, 1, 9000)), AUTO, None),
+        "short_only": (spec(batch=16, prefix_len=500, fixed_suffix=(1,) * 8 + (5,) * 7 + (32,)), AUTO, None),
         "folded": (spec(n_q=32, n_kv=8, head_dim=64, batch=65, prefix_len=256, hot_capacity=256,
                         cold_capacity=24000, fixed_suffix=tuple(max(1, n) for n in _fold_lengths(65))),
                    CASCADE, None),
