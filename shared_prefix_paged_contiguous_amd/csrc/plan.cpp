@@ -159,6 +159,34 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   const int64_t split0 = std::max<int64_t>(
       kMinSplitTokens, round_up(ceil_div(std::max<int64_t>(units, 1), target), kPrefixTile));
   int32_t blocks = split_classes(split0);
+  if (backend == GKV_BACKEND_DENSE && n_classes > 0) {
+    // Dense steps give every slot to prefix work, and the busiest CU sets the
+    // time: k = ceil(blocks / CUs) workgroups of one split length each, two
+    // at a time (a CU with two resident prefix workgroups does about 1.25x
+    // the work per unit time of a CU with one; measured) and the odd last one
+    // alone, plus a fixed cost per workgroup (query rows, ring fill, partial
+    // rows: about eight blocks' worth).  Take the split length with the least
+    // such time; ties go to the fewer workgroups.
+    int64_t lmax = 0;
+    for (int32_t c = 0; c < n_classes; ++c) lmax = std::max<int64_t>(lmax, a.classes[c].len);
+    const int64_t cus = std::max(1, shape.cus);
+    double best = 0.0;
+    int64_t best_st = split0;
+    int32_t best_blocks = 0;
+    for (int64_t ns = 1; ns <= kMaxSplits; ++ns) {
+      const int64_t st = std::max<int64_t>(kMinSplitTokens, round_up(ceil_div(lmax, ns), kPrefixTile));
+      const int32_t nb = split_classes(st);
+      const int64_t k = ceil_div(nb, cus);
+      const double per = static_cast<double>(std::min(st, lmax)) + 8.0 * kHotBlock;   // one workgroup
+      const double t = (k / 2) * 2 * per / 1.25 + (k % 2) * per;
+      if (best_blocks == 0 || t < best || (t == best && nb < best_blocks)) {
+        best = t;
+        best_st = st;
+        best_blocks = nb;
+      }
+    }
+    blocks = split_classes(best_st);
+  }
   // Cascade: when folded suffix pairs (see below) would not fit beside this
   // prefix grid but would beside a somewhat smaller one, lengthen the splits
   // (up to twice) until they fit.
