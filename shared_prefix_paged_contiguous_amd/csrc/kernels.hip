@@ -760,7 +760,8 @@ __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, 
 // gk * G + l / CH and walks the partials itself, NB at a time with all their
 // lse and chunk loads issued together, against a running reference point.
 // One round trip per NB partials for a whole KV head (short requests have
-// few partials per head: their prefix splits and their tile).
+// few partials per head: their prefix splits and their tile); a batch loads
+// only its partials (the count is uniform across the wave).
 template <typename T, int D, typename P>
 __device__ __forceinline__ void join_group(const StepArgs& a, const JoinSrc& src, int b, int gk, int lane) {
   constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
@@ -782,13 +783,18 @@ __device__ __forceinline__ void join_group(const StepArgs& a, const JoinSrc& src
 #pragma unroll
     for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
     for (int base = 0; base < np; base += NB) {
+      const int cnt = min(NB, np - base);
       float lp[NB];
       u32x4 raw[NB];
 #pragma unroll
-      for (int k = 0; k < NB; ++k) {   // indices past the last partial repeat it and weigh zero
-        const int p = min(base + k, np - 1);
-        lp[k] = base + k < np ? load_partial((p < ns ? a.p_lse : a.s_lse) + row_of(p)) : kNegInf;
-        raw[k] = load_partial_chunk(static_cast<const P*>(p < ns ? a.p_o : a.s_o) + row_of(p) * D + EPC * ch);
+      for (int k = 0; k < NB; ++k) {   // slots past the last partial weigh zero
+        lp[k] = kNegInf;
+        raw[k] = u32x4{0u, 0u, 0u, 0u};
+        if (k < cnt) {
+          const int p = base + k;
+          lp[k] = load_partial((p < ns ? a.p_lse : a.s_lse) + row_of(p));
+          raw[k] = load_partial_chunk(static_cast<const P*>(p < ns ? a.p_o : a.s_o) + row_of(p) * D + EPC * ch);
+        }
       }
       float mb = m;
 #pragma unroll
