@@ -24,6 +24,8 @@ roofline of the dominant kernel, cpu_baseline of the float64 oracle).
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import math
 import os
@@ -222,6 +224,23 @@ def stream_ceiling(n_bytes: int = 1 << 30, reps: int = 10):
             "how": "best of %d per grid size over a 1 GiB buffer; copy = torch copy_ (read + write)" % reps}
 
 
+@contextlib.contextmanager
+def no_gc_pauses():
+    """Python's cyclic garbage collector off while steps are enqueued and
+    timed (collected first, re-enabled after).  A full collection over the
+    workload's objects takes 40-50 ms; landing inside a timed loop of 100-200
+    steps, it leaves the GPU idle and inflates the per-step time several
+    times over (measured: one loop in every fresh process without this)."""
+    gc.collect()
+    enabled = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if enabled:
+            gc.enable()
+
+
 def make_workload(args):
     """The named workload, or a variant of it with another batch and/or
     suffix-length range (--batch, --suffix-range LO,HI; e.g. prefix-only
@@ -290,57 +309,58 @@ def run_bench(args):
             return st.run(out, lse, layer=layer, stream=stream)
         return st.step(out, lse, k_new, v_new, slots_new, layer=layer, stream=stream)
 
-    backend = None
-    for i in range(args.warmup):
-        backend = step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        backend = step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    plan = ctx.last_plan()
-    log(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step (host wall {wall*1e6/args.steps:.1f} us/step), "
-        f"backend={binding.BACKEND_NAMES[backend]}")
-
-    # same-layer ("warm", cache-resident) timing, reported for contrast only
-    ms_warm = None
-    if not args.no_warm:
+    with no_gc_pauses():
+        backend = None
+        for i in range(args.warmup):
+            backend = step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
         e0.record(stream)
         for i in range(args.steps):
-            step(i, layer=0)
+            backend = step(i)
         e1.record(stream)
         torch.cuda.synchronize()
-        ms_warm = e0.elapsed_time(e1) / args.steps
+        wall = time.perf_counter() - t0
+        ms_step = e0.elapsed_time(e1) / args.steps
+        plan = ctx.last_plan()
+        log(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step (host wall {wall*1e6/args.steps:.1f} us/step), "
+            f"backend={binding.BACKEND_NAMES[backend]}")
 
-    # gkv_cold_append alone: the batch's new token rows into their slots
-    e0.record(stream)
-    for i in range(args.steps):
-        ctx.cold_append(i % replicas, k_new, v_new, slots_new, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us_append = e0.elapsed_time(e1) / args.steps * 1e3
+        # same-layer ("warm", cache-resident) timing, reported for contrast only
+        ms_warm = None
+        if not args.no_warm:
+            e0.record(stream)
+            for i in range(args.steps):
+                step(i, layer=0)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_warm = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel durations with HIP events recorded by the library on this stream
-    ctx.kernel_timing(args.steps)
-    for i in range(args.steps):
-        step(i)
-    per = ctx.kernel_timing_read(args.steps)
-    ctx.kernel_timing(0)
+        # gkv_cold_append alone: the batch's new token rows into their slots
+        e0.record(stream)
+        for i in range(args.steps):
+            ctx.cold_append(i % replicas, k_new, v_new, slots_new, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_append = e0.elapsed_time(e1) / args.steps * 1e3
 
-    # host cost of a step inside the library (validation, planning, launch),
-    # read after each call: the pages' dispatch-overhead claim is about this
-    plan_us, call_us = [], []
-    for i in range(args.steps):
-        step(i)
-        p = ctx.last_plan()
-        plan_us.append(p["host_plan_us"])
-        call_us.append(p["host_call_us"])
-    torch.cuda.synchronize()
+        # per-kernel durations with HIP events recorded by the library on this stream
+        ctx.kernel_timing(args.steps)
+        for i in range(args.steps):
+            step(i)
+        per = ctx.kernel_timing_read(args.steps)
+        ctx.kernel_timing(0)
+
+        # host cost of a step inside the library (validation, planning, launch),
+        # read after each call: the pages' dispatch-overhead claim is about this
+        plan_us, call_us = [], []
+        for i in range(args.steps):
+            step(i)
+            p = ctx.last_plan()
+            plan_us.append(p["host_plan_us"])
+            call_us.append(p["host_call_us"])
+        torch.cuda.synchronize()
     host = {"plan_us_median": round(float(np.median(plan_us)), 3),
             "call_us_median": round(float(np.median(call_us)), 3),
             "call_us_p90": round(float(np.percentile(call_us, 90)), 3),
@@ -437,11 +457,12 @@ def timeline(args):
     buf = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
     st.ctx.step_trace(buf)
     runs = []
-    for i in range(args.tl_steps):
-        buf.zero_()
-        st.step(out, lse, k_new, v_new, slots, layer=i % replicas)
-        torch.cuda.synchronize()
-        runs.append(buf.cpu().numpy().reshape(grid, 4).astype(np.int64))
+    with no_gc_pauses():
+        for i in range(args.tl_steps):
+            buf.zero_()
+            st.step(out, lse, k_new, v_new, slots, layer=i % replicas)
+            torch.cuda.synchronize()
+            runs.append(buf.cpu().numpy().reshape(grid, 4).astype(np.int64))
     st.ctx.step_trace(None)
 
     n_kv = w.spec.n_kv
@@ -511,12 +532,13 @@ def fit_msat(args):
     def time_step(w, force, n_layers=2, warm=5, steps=20):
         st = DecodeState(w, n_layers=n_layers, force_backend=force)
         out, lse = st.new_outputs()
-        for i in range(warm):
-            st.run(out, lse, layer=i % n_layers)
-        st.ctx.kernel_timing(steps)
-        for i in range(steps):
-            st.run(out, lse, layer=i % n_layers)
-        us = float(st.ctx.kernel_timing_read(steps).mean()) * 1e3
+        with no_gc_pauses():
+            for i in range(warm):
+                st.run(out, lse, layer=i % n_layers)
+            st.ctx.kernel_timing(steps)
+            for i in range(steps):
+                st.run(out, lse, layer=i % n_layers)
+            us = float(st.ctx.kernel_timing_read(steps).mean()) * 1e3
         del st
         torch.cuda.empty_cache()
         return us
@@ -587,12 +609,13 @@ def paged_comparator(args):
         out = torch.empty((bsz, n_q, d), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((bsz, n_q), dtype=torch.float32, device="cuda")
         run = lambda i: ctx.attn_decode(i % layers, q, ids, indptr, None, indices_d, out, lse)
-        for i in range(3):
-            run(i)
-        ctx.kernel_timing(reps)
-        for i in range(reps):
-            run(i)
-        us = float(ctx.kernel_timing_read(reps).mean()) * 1e3
+        with no_gc_pauses():
+            for i in range(3):
+                run(i)
+            ctx.kernel_timing(reps)
+            for i in range(reps):
+                run(i)
+            us = float(ctx.kernel_timing_read(reps).mean()) * 1e3
         ctx.kernel_timing(0)
         return us, out, lse
 
@@ -735,13 +758,14 @@ def multi_prefix(args):
         st = DecodeState(w, n_layers=replicas, registry=True)
         alg = algorithmic(w, st)
         out, lse = st.new_outputs()
-        for i in range(5):
-            st.run(out, lse, layer=i % replicas)
         steps = args.mp_steps
-        st.ctx.kernel_timing(steps)
-        for i in range(steps):
-            st.run(out, lse, layer=i % replicas)
-        ms = st.ctx.kernel_timing_read(steps)
+        with no_gc_pauses():
+            for i in range(5):
+                st.run(out, lse, layer=i % replicas)
+            st.ctx.kernel_timing(steps)
+            for i in range(steps):
+                st.run(out, lse, layer=i % replicas)
+            ms = st.ctx.kernel_timing_read(steps)
         st.ctx.kernel_timing(0)
         us = float(np.median(ms)) * 1e3
         rs = st.ctx.registry_stats()
