@@ -55,7 +55,7 @@ struct gkv_ctx {
   int32_t dev_cus = gkv::kDefaultCus;
   int32_t dev_xcds = gkv::kDefaultCus / gkv::kCusPerXcd;
   std::string err;
-  gkv::StepArgs args;   // kernel-argument block of the current step (~9 KB)
+  gkv::StepArgs args;   // work description of the current step (~24 KB; launched in the 6 KB form up to 128 requests)
   std::vector<hipEvent_t> timing_events;   // 2 per recorded call (kernel start, end)
   int32_t timing_capacity = 0;
   int32_t timing_used = 0;

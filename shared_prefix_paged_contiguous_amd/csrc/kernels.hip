@@ -51,6 +51,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <cstring>
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
@@ -642,7 +643,8 @@ __device__ __forceinline__ int parts_of(const RankDesc& rd) {
 struct JoinSrc {
   int ns, c0, n_parts;
 };
-__device__ __forceinline__ JoinSrc join_src(const StepArgs& a, int b) {
+template <class A>
+__device__ __forceinline__ JoinSrc join_src(const A& a, int b) {
   const RankDesc rd = a.ranks[table_at(a.rank_of, b)];
   const int cls = table_at(a.req_class, b);
   JoinSrc s;
@@ -685,8 +687,8 @@ __device__ __forceinline__ void unpack_chunk(const u32x4& w, float (&v)[16 / siz
 // partials is a handful of independent loads issued back to back (indices
 // past the last partial repeat it and weigh zero).  The lane groups then sum
 // their chunks with cross-lane adds.
-template <typename T, int D, typename P>
-__device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, int b, int h, int lane) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void join_row(const A& a, const JoinSrc& src, int b, int h, int lane) {
   constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
   constexpr int RPI = 64 / CH;                                 // rows per wave-wide access
   constexpr int EPC = 16 / static_cast<int>(sizeof(P));      // values per chunk
@@ -762,8 +764,8 @@ __device__ __forceinline__ void join_row(const StepArgs& a, const JoinSrc& src, 
 // One round trip per NB partials for a whole KV head (short requests have
 // few partials per head: their prefix splits and their tile); a batch loads
 // only its partials (the count is uniform across the wave).
-template <typename T, int D, typename P>
-__device__ __forceinline__ void join_group(const StepArgs& a, const JoinSrc& src, int b, int gk, int lane) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void join_group(const A& a, const JoinSrc& src, int b, int gk, int lane) {
   constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
   constexpr int HP = 64 / CH;                                  // query heads per pass
   constexpr int EPC = 16 / static_cast<int>(sizeof(P));      // values per chunk
@@ -833,7 +835,8 @@ __device__ __forceinline__ void join_group(const StepArgs& a, const JoinSrc& src
 // agent-scope accesses and waited for them to complete, then the workgroup
 // barrier; only then is the arrival counted, so a count seen by the join
 // workgroup means the partial is in place.
-__device__ __forceinline__ void arrive(const StepArgs& a, int b, int g) {
+template <class A>
+__device__ __forceinline__ void arrive(const A& a, int b, int g) {
   __hip_atomic_fetch_add(a.counters + static_cast<size_t>(b) * a.n_kv + g, 1, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -849,7 +852,8 @@ __device__ __forceinline__ void arrive(const StepArgs& a, int b, int g) {
 // valid.  Taking n off (instead of storing zero) keeps the counters exact
 // for the next call in that case too: the late arrivals of this call still
 // land before the kernel ends, and bring the counter back to zero.
-__device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, int n) {
+template <class A>
+__device__ __forceinline__ void wait_arrivals(const A& a, int b, int g, int n) {
   int32_t* cnt = a.counters + static_cast<size_t>(b) * a.n_kv + g;
   bool arrived = false;
   for (int it = 0; it < a.spin_limit; ++it) {
@@ -869,7 +873,8 @@ __device__ __forceinline__ void wait_arrivals(const StepArgs& a, int b, int g, i
 // ------------------------------------------------------------ timeline
 // Records of gkv_step_trace (see kTraceWords): one thread per workgroup
 // writes its start, a mark and its end.
-__device__ __forceinline__ void trace_start(const StepArgs& a, int blk, uint32_t kind) {
+template <class A>
+__device__ __forceinline__ void trace_start(const A& a, int blk, uint32_t kind) {
   // HW_ID (hardware register 4) and XCC_ID (20), whole 32-bit fields
   const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
   const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xf;
@@ -878,7 +883,8 @@ __device__ __forceinline__ void trace_start(const StepArgs& a, int blk, uint32_t
   r[1] = 0;
   r[3] = (static_cast<uint64_t>(kind) << 32) | (xcc << 16) | (hw & 0xffff);
 }
-__device__ __forceinline__ void trace_mark(const StepArgs& a, int blk) {
+template <class A>
+__device__ __forceinline__ void trace_mark(const A& a, int blk) {
   if (a.trace && threadIdx.x == 0)
     a.trace[static_cast<size_t>(blk) * kTraceWords + 1] = __builtin_amdgcn_s_memrealtime();
 }
@@ -903,7 +909,8 @@ struct SuffixPiece {
   int b, w0, len, tb1, piece;
   bool single;   // the request's slot table is this one part
 };
-__device__ __forceinline__ SuffixPiece suffix_piece(const StepArgs& a, int part, int wave) {
+template <class A>
+__device__ __forceinline__ SuffixPiece suffix_piece(const A& a, int part, int wave) {
   // rank: the last r with ranks[r].part0 <= part, which is the part itself
   // when every request has one part
   int lo = part;
@@ -933,8 +940,8 @@ __device__ __forceinline__ SuffixPiece suffix_piece(const StepArgs& a, int part,
 // wave w joins columns w, w+4, ... and writes the request's output (a
 // request without a HOT prefix whose slot table is this one part) or the
 // part's partial.  Returns true for the former.
-template <typename T, int D, typename P>
-__device__ __forceinline__ bool suffix_publish(const StepArgs& a, SuffixSmem<T, D>& sm, int part, int b,
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ bool suffix_publish(const A& a, SuffixSmem<T, D>& sm, int part, int b,
                                                bool single, int gk, int wave, int lane) {
   constexpr int PER = D / 64;
   const int G = a.group;
@@ -980,8 +987,8 @@ __device__ __forceinline__ void suffix_to_lds(SuffixSmem<T, D>& sm, int wave, in
 // (k_new/v_new row) into its COLD slot; slots outside the pool are skipped.
 // The eight KV-head workgroups of the part write the whole row; nothing else
 // reads that slot in the step.
-template <typename T, int D>
-__device__ __forceinline__ void suffix_copy_new(const StepArgs& a, int b, int gk, int lane) {
+template <typename T, int D, class A>
+__device__ __forceinline__ void suffix_copy_new(const A& a, int b, int gk, int lane) {
   constexpr int CH = D * static_cast<int>(sizeof(T)) / 16;   // 16-byte chunks per row
   static_assert(CH <= 32, "a row copy takes at most half a wave");
   const int slot = a.new_slots[b];
@@ -995,8 +1002,8 @@ __device__ __forceinline__ void suffix_copy_new(const StepArgs& a, int b, int gk
   }
 }
 
-template <typename T, int D, typename P>
-__device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk, uint8_t* smem_raw) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
@@ -1138,8 +1145,8 @@ __device__ __forceinline__ void suffix_part(const StepArgs& a, int part, int gk,
 // Suffix block i: part q = i / n_kv for KV head i % n_kv, or, folded, part
 // n_parts-1-q (the shorter) and then part q; the barrier between the two
 // frees the LDS.  Folded, blocks q >= ceil(n_parts / 2) are grid padding.
-template <typename T, int D, typename P>
-__device__ __forceinline__ void suffix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_raw) {
   const int q = blk / a.n_kv;
   const int gk = blk - q * a.n_kv;
   if (q >= (a.fold ? (a.n_parts + 1) / 2 : a.n_parts)) return;   // grid padding
@@ -1279,8 +1286,8 @@ struct PrefixSmem {
   uint8_t ring[kStages][2 * kImg];
 };
 
-template <typename T, int D, int RB, typename P>
-__device__ __forceinline__ void prefix_block(const StepArgs& a, int blk, uint8_t* smem_raw) {
+template <typename T, int D, int RB, typename P, class A>
+__device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_raw) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using SM = PrefixSmem<T, D>;
@@ -1591,8 +1598,8 @@ constexpr size_t step_smem_bytes() {
 // stores are complete, one thread per KV head waits for the head's prefix
 // splits.  Join: wave w joins KV heads w, w + 4, ... (join_group).  The
 // tiles need no prefix result, so with free slots they run beside it.
-template <typename T, int D, typename P>
-__device__ __forceinline__ void short_join(const StepArgs& a, int r, int blk) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void short_join(const A& a, int r, int blk) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
@@ -1675,8 +1682,8 @@ __device__ __forceinline__ void short_join(const StepArgs& a, int r, int blk) {
 // heads g*G + w, g*G + w + 4, ...  Where the partials lie is read before the
 // wait, so after it only the partials themselves are loaded.  The rest: one
 // short request each.
-template <typename T, int D, typename P>
-__device__ __forceinline__ void join_block(const StepArgs& a, int j) {
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ void join_block(const A& a, int j) {
   const int blk = a.prefix_blocks + a.suffix_blocks + j;
   const int nj = a.inline_rank0 * a.n_kv;
   if (j >= nj) {
@@ -1697,9 +1704,9 @@ __device__ __forceinline__ void join_block(const StepArgs& a, int j) {
 
 // Two workgroups per CU; fp32 rows of 128 take 96 KB of LDS per prefix
 // workgroup, so one.
-template <typename T, int D, int RB, typename P>
+template <typename T, int D, int RB, typename P, class A>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && D == 128 ? 1 : 2))) void step_kernel(StepArgs a) {
+__attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && D == 128 ? 1 : 2))) void step_kernel(A a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[step_smem_bytes<T, D>()];
   if (a.tail != kArgsTail) return;   // the work description did not arrive whole
   const int blk = blockIdx.x;
@@ -1730,8 +1737,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, co
   }
 }
 
-template <typename T, int D>
-hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
+template <typename T, int D, class A>
+hipError_t launch_typed(const A& a, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
   // With timing events, the kernel is launched through hipExtLaunchKernelGGL,
   // which stamps the events with the kernel's own start and end.
   hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
@@ -1741,19 +1748,19 @@ hipError_t launch_typed(const StepArgs& a, int32_t backend, hipStream_t stream, 
     // bf16 inputs: partial rows in fp32 or in bf16, 64- or 128-row prefix tiles
     if (a.partial_f32) {
       if (a.rb == 2)
-        hipExtLaunchKernelGGL(step_kernel<T, D, 2, float>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+        hipExtLaunchKernelGGL(step_kernel<T, D, 2, float, A>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
       else
-        hipExtLaunchKernelGGL(step_kernel<T, D, 1, float>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+        hipExtLaunchKernelGGL(step_kernel<T, D, 1, float, A>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     } else {
       if (a.rb == 2)
-        hipExtLaunchKernelGGL(step_kernel<T, D, 2, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+        hipExtLaunchKernelGGL(step_kernel<T, D, 2, T, A>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
       else
-        hipExtLaunchKernelGGL(step_kernel<T, D, 1, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+        hipExtLaunchKernelGGL(step_kernel<T, D, 1, T, A>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
     }
   } else {
     // fp32 inputs: fp32 partials, 64-row tiles
     if (a.rb != 1 || !a.partial_f32) return hipErrorInvalidValue;
-    hipExtLaunchKernelGGL(step_kernel<T, D, 1, T>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(step_kernel<T, D, 1, T, A>, dim3(blocks), dim3(kThreads), 0, stream, e0, e1, 0, a);
   }
   return hipGetLastError();
 }
@@ -1864,14 +1871,30 @@ hipError_t launch_hot_write(const void* k_rows, const void* v_rows, int32_t n, i
   return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
-                       hipEvent_t* ev) {
+namespace {
+template <class A>
+hipError_t launch_sized(const A& a, int32_t dtype, int32_t backend, hipStream_t stream, hipEvent_t* ev) {
   if (dtype == 1) {
     return a.head_dim == 128 ? launch_typed<__bf16, 128>(a, backend, stream, ev)
                              : launch_typed<__bf16, 64>(a, backend, stream, ev);
   }
   return a.head_dim == 128 ? launch_typed<float, 128>(a, backend, stream, ev)
                            : launch_typed<float, 64>(a, backend, stream, ev);
+}
+}  // namespace
+
+hipError_t launch_step(const StepArgs& a, int32_t dtype, int32_t backend, hipStream_t stream,
+                       hipEvent_t* ev) {
+  if (a.batch > kSmallBatch) return launch_sized(a, dtype, backend, stream, ev);
+  // the small form: the head and the first kSmallBatch entries of each table
+  StepArgsSmall s;
+  static_cast<StepHead&>(s) = static_cast<const StepHead&>(a);
+  std::memcpy(s.ranks, a.ranks, sizeof(s.ranks));
+  std::memcpy(s.rank_of, a.rank_of, sizeof(s.rank_of));
+  std::memcpy(s.members, a.members, sizeof(s.members));
+  std::memcpy(s.req_class, a.req_class, sizeof(s.req_class));
+  s.tail = a.tail;
+  return launch_sized(s, dtype, backend, stream, ev);
 }
 
 }  // namespace gkv

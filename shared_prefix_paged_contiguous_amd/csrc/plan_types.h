@@ -1,8 +1,10 @@
 // Work description of one decode step, shared by the host planner and the
 // device kernels.  The whole description travels in the kernel arguments
-// (about 24 KB), so a step needs no host-to-device copy before its kernels.
+// (about 24 KB, or 6 KB for a batch of at most 128), so a step needs no
+// host-to-device copy before its kernels.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 namespace gkv {
@@ -117,7 +119,12 @@ struct RankDesc {
   int32_t req;          // the request (batch index)
 };
 
-struct StepArgs {
+// The work description, in two parts: StepHead (sizes, pointers, classes)
+// and the per-request tables sized for MB requests.  The kernel arguments
+// carry the whole of it; a step of at most kSmallBatch requests is
+// launched with the small form (about 6 KB instead of 24 KB), which takes
+// less host time per launch and less time to reach the device.
+struct StepHead {
   int32_t batch, n_q, n_kv, group, head_dim;
   float scale_log2;            // log2(e) / sqrt(head_dim)
   int32_t xcds;                // XCDs of the device (prefix blocks of one group share one)
@@ -161,15 +168,22 @@ struct StepArgs {
   int32_t* status;             // status word: joins that gave up waiting (gkv_step_status)
   uint64_t* trace;             // per-workgroup timeline records (kTraceWords each), null: off
   ClassDesc classes[kMaxClasses];
-  alignas(16) RankDesc ranks[kMaxBatch];   // by rank
+};
+
+template <int MB>
+struct StepArgsT : StepHead {
+  alignas(16) RankDesc ranks[MB];   // by rank
   // small-int tables, 4-byte aligned so entries can be read with 32-bit loads
-  alignas(4) int16_t rank_of[kMaxBatch];   // rank of request b
-  alignas(4) int16_t members[kMaxBatch];   // requests grouped by class
-  alignas(4) int8_t req_class[kMaxBatch];  // class of request b, -1 = none
+  alignas(4) int16_t rank_of[MB];   // rank of request b
+  alignas(4) int16_t members[MB];   // requests grouped by class
+  alignas(4) int8_t req_class[MB];  // class of request b, -1 = none
   // last word: the kernels do nothing unless it holds kArgsTail, so a work
   // description that did not arrive whole is never acted on
   int32_t tail;
 };
+constexpr int kSmallBatch = 128;
+using StepArgs = StepArgsT<kMaxBatch>;
+using StepArgsSmall = StepArgsT<kSmallBatch>;
 constexpr int32_t kArgsTail = 0x47'4b'56'31;
 
 // Status word of a workspace (one 256-byte line after the counters): the

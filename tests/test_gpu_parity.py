@@ -184,6 +184,22 @@ def test_largest_batch_parity(force):
     check(out, lse, *oracle_ref(w))
 
 
+@pytest.mark.parametrize("batch", [127, 128, 129])
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_argument_forms_at_their_edge(batch, force):
+    """Steps of up to 128 requests launch with the small argument block, larger
+    ones with the full one: both sides of the edge, with every table entry in
+    use (short, long and prefix-only requests, last request long)."""
+    lens = [(i * 37) % 90 for i in range(batch)]
+    lens[-1] = 300
+    s = spec(n_q=16, n_kv=4, head_dim=128, batch=batch, prefix_len=500, hot_capacity=512,
+             fixed_suffix=tuple(lens), cold_capacity=16384)
+    w = workloads.make(s)
+    st, out, lse, backend = run(w, force=force)
+    assert backend == force
+    check(out, lse, *oracle_ref(w))
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_most_query_heads_parity(force):
     """The most query heads a context takes (256), 16 per KV head."""
