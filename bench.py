@@ -429,6 +429,11 @@ def run_bench(args):
     return res
 
 
+def _median_or_none(xs):
+    xs = [x for x in xs if x is not None]
+    return round(float(np.median(xs)), 2) if xs else None
+
+
 def timeline(args):
     """Per-workgroup timeline of the step kernel (gkv_step_trace) on the
     bench workload: each workgroup's start, mid-point mark and end from the
@@ -494,6 +499,18 @@ def timeline(args):
             d["duration_p50"] = round(float(np.median(stats_m)), 2)
             row[name] = d
         row["prefix_on_named_xcd"] = float(np.mean(xcc[pre] == (idx[pre] % xcds))) if pre.any() else None
+        # median end per XCD (prefix splits, suffix workgroups) and per KV head
+        # (suffix workgroups: block i of the suffix runs KV head i mod n_kv)
+        by = {}
+        for name, m in (("prefix", pre), ("suffix", suf)):
+            if m.any():
+                by[name + "_end_by_xcd"] = [round(float(np.median(us(rec[m & (xcc == x), 2]))), 2)
+                                            if (m & (xcc == x)).any() else None for x in range(xcds)]
+        if suf.any():
+            head = (idx - plan["n_prefix_blocks"]) % n_kv
+            by["suffix_end_by_kv_head"] = [round(float(np.median(us(rec[suf & (head == h), 2]))), 2)
+                                           for h in range(n_kv)]
+        row["ends"] = by
         # running workgroups per kind in 2 us bins
         edges = np.arange(0.0, row["span_us"] + 2.0, 2.0)
         act = {}
@@ -510,7 +527,10 @@ def timeline(args):
            "span_us_all": sorted(round(r["span_us"], 2) for r in stats), "median_step": med,
            "note": "times in us from the step's first workgroup start (s_memrealtime, 100 MHz); "
                    "[min, median, max] over workgroups; prefix mark = end of the block loop, "
-                   "suffix mark = end of the first part of a folded pair, join mark = end of the wait"}
+                   "suffix mark = end of the first part of a folded pair, join mark = end of the wait",
+           "ends_median_over_steps": {k: [_median_or_none([r["ends"][k][i] for r in stats])
+                                          for i in range(len(stats[0]["ends"][k]))]
+                                      for k in stats[0]["ends"]}}
     print(json.dumps(res), flush=True)
 
 
@@ -790,7 +810,10 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # an idle GPU runs at lowered clocks and takes some tens of milliseconds
+    # of steady load to reach its working clock: 600 steps of the default
+    # workload are about 33 ms
+    ap.add_argument("--warmup", type=int, default=600)
     ap.add_argument("--workload", default="llama8b_lp16k_b64")
     ap.add_argument("--backend", default="auto", choices=["auto", "cascade", "dense"])
     ap.add_argument("--batch", type=int, default=0,

@@ -115,7 +115,11 @@ const char* gkv_last_error(const gkv_ctx* ctx);
  *                  Head-major, so one (head, prefix) slab is one linear run
  *                  of whole blocks.  Write rows with gkv_hot_write.
  *   k_cold, v_cold [C_cold][n_kv][head_dim]  token-major: one slot holds one
- *                  token of every KV head; written with gkv_cold_append.
+ *                  token of every KV head, the row of head g at position
+ *                  g ^ (slot & m), m = (largest power of two dividing n_kv)
+ *                  - 1 (heads permuted within aligned groups of m + 1, so a
+ *                  head's rows are spread over the in-slot offsets); written
+ *                  with gkv_cold_append.  Odd n_kv: position g.
  * Prefix ids, HOT offsets and COLD slots are shared by all layers.  NULL is
  * allowed for a pool that holds no block / slot. */
 int gkv_bind_layer(gkv_ctx* ctx, int32_t layer, void* k_hot, void* v_hot,
@@ -253,8 +257,9 @@ int gkv_registry_stats(const gkv_ctx* ctx, gkv_registry_counts* out);
 
 /* Append decoded tokens into COLD (paperlayer.ai §1 "Design": COLD holds
  * suffix and decoded tokens).  k_new, v_new: dev [n][n_kv][head_dim];
- * slots_dev: dev int32 [n].  Row slots[i] of layer `layer`'s k_cold/v_cold
- * becomes a byte copy of row i; other rows are untouched.  Slots outside
+ * slots_dev: dev int32 [n].  Slot slots[i] of layer `layer`'s k_cold/v_cold
+ * becomes a byte copy of row i, its KV heads at their in-slot positions
+ * (gkv_bind_layer); other slots are untouched.  Slots outside
  * [0, C_cold) are skipped on the device (the host cannot read them); repeated
  * slots in one call leave one of the rows, unspecified which.  Asynchronous
  * on `stream`. */

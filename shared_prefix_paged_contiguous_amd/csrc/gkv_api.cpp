@@ -365,10 +365,9 @@ int gkv_cold_append(gkv_ctx* ctx, int32_t layer, const void* k_new, const void* 
     return fail(ctx, GKV_ERR_INVALID, "cold_append: rows must be 16-byte aligned");
   if (ctx->cfg.cold_capacity_tokens == 0) return fail(ctx, GKV_ERR_INVALID, "COLD pool is empty");
   const Layer& L = ctx->layers[layer];
-  const int64_t row_bytes =
-      static_cast<int64_t>(ctx->cfg.n_kv_heads) * ctx->cfg.head_dim * static_cast<int64_t>(elem_size(ctx->cfg));
-  hipError_t e = gkv::launch_cold_append(k_new, v_new, slots_dev, n, L.k_cold, L.v_cold, row_bytes,
-                                         static_cast<int32_t>(ctx->cfg.cold_capacity_tokens),
+  const int64_t head_bytes = static_cast<int64_t>(ctx->cfg.head_dim) * elem_size(ctx->cfg);
+  hipError_t e = gkv::launch_cold_append(k_new, v_new, slots_dev, n, L.k_cold, L.v_cold, ctx->cfg.n_kv_heads,
+                                         head_bytes, static_cast<int32_t>(ctx->cfg.cold_capacity_tokens),
                                          static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_fail(ctx, "cold_append launch", e);
   return GKV_OK;
@@ -639,6 +638,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   a.k_cold = L.k_cold;
   a.v_cold = L.v_cold;
   a.cold_cap = static_cast<int32_t>(c.cold_capacity_tokens);
+  a.cold_mask = gkv::cold_mask_for(c.n_kv_heads);
   a.cold_indices = cold_indices_d;
   a.k_new = k_new;
   a.v_new = k_new ? v_new : nullptr;

@@ -9,10 +9,12 @@
 
 namespace gkv {
 
-// Byte copy of n token rows (row_bytes each, a multiple of 16) into the COLD
-// pool rows named by slots (dev); slots outside [0, cold_cap) are skipped.
+// Byte copy of n token rows (n_kv head rows of head_bytes each, a multiple
+// of 16) into the COLD slots named by slots (dev), head g of a row into
+// position cold_row_pos(g, slot, cold_mask_for(n_kv)) of its slot; slots
+// outside [0, cold_cap) are skipped.
 hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_t* slots,
-                              int32_t n, void* k_cold, void* v_cold, int64_t row_bytes,
+                              int32_t n, void* k_cold, void* v_cold, int32_t n_kv, int64_t head_bytes,
                               int32_t cold_cap, hipStream_t stream);
 
 // Scatter n token rows ([n][n_kv][head_dim]) into the blocked HOT layout,

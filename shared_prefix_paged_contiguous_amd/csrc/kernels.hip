@@ -994,7 +994,7 @@ __device__ __forceinline__ void suffix_copy_new(const A& a, int b, int gk, int l
   const int slot = a.new_slots[b];
   if (slot >= 0 && slot < a.cold_cap) {
     const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
-    const size_t dst = (static_cast<size_t>(slot) * a.n_kv + gk) * D;
+    const size_t dst = (static_cast<size_t>(slot) * a.n_kv + cold_row_pos(gk, slot, a.cold_mask)) * D;
     const int ch = lane & 31;
     const T* src = static_cast<const T*>(lane < 32 ? a.k_new : a.v_new) + new_row;
     T* to = static_cast<T*>(const_cast<void*>(lane < 32 ? a.k_cold : a.v_cold)) + dst;
@@ -1028,8 +1028,9 @@ __device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_
   for (int k = 0; k < D / 4; ++k) o[k] = 0.f;
   if (len > 0) {
     const size_t stride = static_cast<size_t>(a.n_kv) * D;
-    const T* kc = static_cast<const T*>(a.k_cold) + gk * D;
-    const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
+    const T* kc = static_cast<const T*>(a.k_cold);
+    const T* vc = static_cast<const T*>(a.v_cold) + TR::EPB * n;
+    const int mask = a.cold_mask;
     const int n_tiles = (len + kSuffixTile - 1) / kSuffixTile;
     const int cap1 = a.cold_cap - 1;
     // Fused decode step: the wave whose piece ends the slot table reads the
@@ -1071,7 +1072,8 @@ __device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_
     // below the QK^T of the tile, which waits for K, so each tile cost two
     // memory round trips.
     auto row = [&](const T* pool, const T* fresh_row, int id) {
-      const T* p = pool + static_cast<size_t>(max(id, 0)) * stride;
+      const int s = max(id, 0);
+      const T* p = pool + static_cast<size_t>(s) * stride + cold_row_pos(gk, s, mask) * D;
       return id < 0 ? fresh_row : p;
     };
     auto load_kv = [&](int i, KOp (&k0)[TR::KS], KOp (&k1)[TR::KS], VVec (&v)[8]) {
@@ -1632,8 +1634,8 @@ __device__ __forceinline__ void short_join(const A& a, int r, int blk) {
       st.init();
       if (col_ok) TR::load_row(st.q, static_cast<const T*>(a.q) + (static_cast<size_t>(b) * a.n_q + h) * D, g);
       else TR::zero_row(st.q);
-      const T* kc = static_cast<const T*>(a.k_cold) + gk * D;
-      const T* vc = static_cast<const T*>(a.v_cold) + gk * D + TR::EPB * n;
+      const T* kc = static_cast<const T*>(a.k_cold);
+      const T* vc = static_cast<const T*>(a.v_cold) + TR::EPB * n;
       const size_t new_row = (static_cast<size_t>(b) * a.n_kv + gk) * D;
       const T* knew = static_cast<const T*>(a.k_new) + new_row;
       const T* vnew = static_cast<const T*>(a.v_new) + new_row + TR::EPB * n;
@@ -1641,7 +1643,7 @@ __device__ __forceinline__ void short_join(const A& a, int r, int blk) {
       // entry; the tile masks them)
       auto row = [&](const T* pool, const T* fresh_row, int i) {
         const int t = __shfl(id, min(i, len - 1));
-        return t < 0 ? fresh_row : pool + static_cast<size_t>(t) * stride;
+        return t < 0 ? fresh_row : pool + static_cast<size_t>(t) * stride + cold_row_pos(gk, t, a.cold_mask) * D;
       };
       KOp k0[TR::KS], k1[TR::KS];
       VVec v[8];
@@ -1722,18 +1724,27 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && D == 128 ? 1 : 2))) void st
   }
 }
 
+// Chunk ch of input row tok (head ch / head_chunks) goes to the same chunk
+// of that head's position in slot slots[tok].
 __global__ __launch_bounds__(kThreads) void append_kernel(const u32x4* k_new, const u32x4* v_new,
                                                           const int32_t* slots, int32_t n,
                                                           u32x4* k_cold, u32x4* v_cold,
-                                                          int64_t row_chunks, int32_t cold_cap) {
+                                                          int32_t head_chunks, int32_t n_kv,
+                                                          int32_t cold_cap) {
+  const int64_t row_chunks = static_cast<int64_t>(head_chunks) * n_kv;
+  const int32_t mask = cold_mask_for(n_kv);
   const int64_t total = static_cast<int64_t>(n) * row_chunks;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t tok = i / row_chunks, ch = i % row_chunks;
+    const int64_t tok = i / row_chunks;
+    const int32_t ch = static_cast<int32_t>(i - tok * row_chunks);
     const int32_t s = slots[tok];
     if (s < 0 || s >= cold_cap) continue;
-    k_cold[static_cast<int64_t>(s) * row_chunks + ch] = k_new[i];
-    v_cold[static_cast<int64_t>(s) * row_chunks + ch] = v_new[i];
+    const int32_t g = ch / head_chunks;
+    const int64_t dst = static_cast<int64_t>(s) * row_chunks +
+                        static_cast<int64_t>(cold_row_pos(g, s, mask)) * head_chunks + (ch - g * head_chunks);
+    k_cold[dst] = k_new[i];
+    v_cold[dst] = v_new[i];
   }
 }
 
@@ -1839,16 +1850,18 @@ hipError_t launch_stream_read(const void* p, size_t bytes, int32_t workgroups, u
 }
 
 hipError_t launch_cold_append(const void* k_new, const void* v_new, const int32_t* slots, int32_t n,
-                              void* k_cold, void* v_cold, int64_t row_bytes, int32_t cold_cap,
+                              void* k_cold, void* v_cold, int32_t n_kv, int64_t head_bytes, int32_t cold_cap,
                               hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t row_chunks = row_bytes / 16;
+  if (n_kv <= 0 || head_bytes <= 0 || head_bytes % 16) return hipErrorInvalidValue;
+  const int32_t head_chunks = static_cast<int32_t>(head_bytes / 16);
+  const int64_t row_chunks = static_cast<int64_t>(head_chunks) * n_kv;
   const int64_t total = static_cast<int64_t>(n) * row_chunks;
   const int64_t blocks = (total + kThreads - 1) / kThreads;
   const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);
   append_kernel<<<grid, kThreads, 0, stream>>>(
       static_cast<const u32x4*>(k_new), static_cast<const u32x4*>(v_new), slots, n,
-      static_cast<u32x4*>(k_cold), static_cast<u32x4*>(v_cold), row_chunks, cold_cap);
+      static_cast<u32x4*>(k_cold), static_cast<u32x4*>(v_cold), head_chunks, n_kv, cold_cap);
   return hipGetLastError();
 }
 

@@ -152,7 +152,7 @@ struct StepHead {
   const void* k_cold;
   const void* v_cold;
   int32_t cold_cap;
-  int32_t pad2_;
+  int32_t cold_mask;           // in-slot placement of KV-head rows: cold_row_pos
   const int32_t* cold_indices; // dev
   // fused decode step (null otherwise): request b's new token, the last
   // entry of its slot table, is read from k_new/v_new [B][n_kv][head_dim]
@@ -185,6 +185,16 @@ constexpr int kSmallBatch = 128;
 using StepArgs = StepArgsT<kMaxBatch>;
 using StepArgsSmall = StepArgsT<kSmallBatch>;
 constexpr int32_t kArgsTail = 0x47'4b'56'31;
+
+// COLD in-slot layout: slot s holds the row of KV head g at position
+// g ^ (s & mask), mask = (largest power of two dividing n_kv) - 1.  A KV
+// head's rows thus sit at every position of their aligned group, not at one
+// fixed offset: gathering 256-byte head rows that all lie 256 bytes past a
+// 1 KB boundary ran measurably slower than the other offsets on gfx950, and
+// with a fixed position every request's joins waited for those heads.
+constexpr int32_t cold_mask_for(int32_t n_kv) { return (n_kv & -n_kv) - 1; }
+// (constexpr functions serve host and device code alike)
+constexpr int32_t cold_row_pos(int32_t g, int32_t slot, int32_t mask) { return g ^ (slot & mask); }
 
 // Status word of a workspace (one 256-byte line after the counters): the
 // number of joins that stopped waiting for their partials at the spin limit

@@ -39,11 +39,14 @@ def spec(**kw):
 
 
 # --------------------------------------------------------------- cold append
+@pytest.mark.parametrize("n_kv,d", [(2, 64), (3, 64), (8, 128), (12, 64)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_cold_append_bit_exact(dtype):
+def test_cold_append_bit_exact(dtype, n_kv, d):
+    """Whole pools after gkv_cold_append against the oracle's model of the
+    COLD slot layout (heads permuted within a slot by its index)."""
     torch.manual_seed(0)
-    n_kv, d, cap = 2, 64, 300
-    ctx = binding.Context(8, n_kv, d, dtype, 0, cap)
+    cap = 300
+    ctx = binding.Context(2 * n_kv, n_kv, d, dtype, 0, cap)
     td = torch.float32 if dtype == "f32" else torch.bfloat16
     k_cold = torch.randn(cap, n_kv, d).to(td).cuda()
     v_cold = torch.randn(cap, n_kv, d).to(td).cuda()
@@ -154,7 +157,8 @@ def test_ragged_multi_tile_parity(force):
     check(out, lse, *oracle_ref(w))
 
 
-@pytest.mark.parametrize("n_q,n_kv,d", [(8, 8, 128), (16, 1, 128), (10, 2, 128), (32, 8, 64), (20, 4, 64)])
+@pytest.mark.parametrize("n_q,n_kv,d", [(8, 8, 128), (16, 1, 128), (10, 2, 128), (32, 8, 64), (20, 4, 64),
+                                         (6, 3, 128), (24, 12, 64)])
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_group_and_head_dim_parity(n_q, n_kv, d, force):
     s = spec(n_q=n_q, n_kv=n_kv, head_dim=d, batch=5, prefix_len=333, hot_capacity=400,
@@ -522,9 +526,12 @@ def test_fused_step_equals_append_then_attend(case):
     assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
     for i in (2, 3):                                  # k_cold, v_cold
         assert torch.equal(_bits(sa.pools[0][i]), _bits(sb.pools[0][i]))
-    # the appended rows are the new ones
-    assert torch.equal(_bits(sb.pools[0][2][slots.long()]), _bits(k_new))
-    assert torch.equal(_bits(sb.pools[0][3][slots.long()]), _bits(v_new))
+    # the appended slots hold the new rows, each KV head at its in-slot
+    # position (the oracle's model of the COLD layout)
+    for i, new in ((2, k_new), (3, v_new)):
+        pool = _bits(sb.pools[0][i]).cpu().numpy()
+        want = append_model(pool, sa.last_slots(), _bits(new).cpu().numpy())
+        assert pool.tobytes() == want.tobytes()
 
 
 def test_fused_step_repeats_and_matches_the_oracle():

@@ -14,7 +14,7 @@ from hypothesis import given, settings
 from hypothesis import strategies as st
 
 from oracle.alloc import ColdAllocModel, HotAllocModel, NoSpace, NotFound
-from oracle.append import append_model
+from oracle.append import append_model, slot_position
 from oracle.dispatch import BACKEND_CASCADE, BACKEND_DENSE, choose_backend, m_eff
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -180,12 +180,61 @@ def test_append_scatter():
     pool = np.arange(5 * 2 * 3, dtype=np.float32).reshape(5, 2, 3)
     rows = -np.arange(2 * 2 * 3, dtype=np.float32).reshape(2, 2, 3) - 1
     out = append_model(pool, [3, 1], rows)
-    assert np.array_equal(out[3], rows[0]) and np.array_equal(out[1], rows[1])
+    # n_kv = 2: odd slots hold their two heads swapped
+    assert out[3].tolist() == [[-4.0, -5.0, -6.0], [-1.0, -2.0, -3.0]]
+    assert out[1].tolist() == [[-10.0, -11.0, -12.0], [-7.0, -8.0, -9.0]]
     for r in (0, 2, 4):
         assert out[r].tobytes() == pool[r].tobytes()
     assert pool[3, 0, 0] == 18.0          # input untouched
-    out = append_model(pool, [2, 2], rows)  # repeated slot: last write wins
+    out = append_model(pool, [2, 2], rows)  # repeated slot: last write wins; even slot: in order
     assert np.array_equal(out[2], rows[1])
+
+
+# in-slot position of head g, tabulated by hand from the layout's statement
+# (head g at g XOR (slot mod P), P the largest power of two dividing n_kv)
+SLOT_POSITIONS = {
+    # (n_kv, slot): positions of heads 0, 1, ...
+    (1, 7): [0],
+    (3, 5): [0, 1, 2],                     # odd n_kv: P = 1
+    (2, 4): [0, 1],
+    (2, 9): [1, 0],
+    (4, 6): [2, 3, 0, 1],                  # 6 mod 4 = 2
+    (4, 8): [0, 1, 2, 3],
+    (6, 3): [1, 0, 3, 2, 5, 4],            # P = 2
+    (8, 13): [5, 4, 7, 6, 1, 0, 3, 2],     # 13 mod 8 = 5
+    (12, 7): [3, 2, 1, 0, 7, 6, 5, 4, 11, 10, 9, 8],   # P = 4, 7 mod 4 = 3
+    (16, 21): [5, 4, 7, 6, 1, 0, 3, 2, 13, 12, 15, 14, 9, 8, 11, 10],
+    # slots where a mask of n_kv - 1 would differ from P - 1
+    (6, 4): [0, 1, 2, 3, 4, 5],
+    (12, 8): [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11],
+    (10, 3): [1, 0, 3, 2, 5, 4, 7, 6, 9, 8],
+}
+
+
+@pytest.mark.parametrize("key", sorted(SLOT_POSITIONS))
+def test_slot_positions_tabulated(key):
+    n_kv, slot = key
+    assert [slot_position(g, slot, n_kv) for g in range(n_kv)] == SLOT_POSITIONS[key]
+
+
+def test_append_places_each_head_once():
+    """Every slot holds each head's row exactly once, at the tabulated
+    positions (4 KV heads), and reading back through the positions restores
+    the rows."""
+    rng = np.random.default_rng(3)
+    n_kv, d, cap = 4, 5, 16
+    pool = rng.standard_normal((cap, n_kv, d))
+    slots = [6, 0, 13, 8]
+    rows = rng.standard_normal((len(slots), n_kv, d))
+    out = append_model(pool, slots, rows)
+    assert out[6, 2].tolist() == rows[0, 0].tolist() and out[6, 0].tolist() == rows[0, 2].tolist()
+    for i, s in enumerate(slots):
+        got = sorted(map(tuple, out[s].tolist()))
+        assert got == sorted(map(tuple, rows[i].tolist()))
+        for g in range(n_kv):
+            assert np.array_equal(out[s, slot_position(g, s, n_kv)], rows[i, g])
+    untouched = [r for r in range(cap) if r not in slots]
+    assert np.array_equal(out[untouched], pool[untouched])
 
 
 # ------------------------------------------------------------------ dispatch
