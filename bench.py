@@ -549,7 +549,9 @@ def fit_msat(args):
     from shared_prefix_paged_contiguous_amd import binding, workloads
     from shared_prefix_paged_contiguous_amd.harness import DecodeState
 
-    def time_step(w, force, n_layers=2, warm=5, steps=20):
+    def time_step(w, force, n_layers=2, warm=200, steps=20):
+        # warm-up long enough for the clocks to settle after the host-side
+        # set-up of each point (tens of milliseconds of load)
         st = DecodeState(w, n_layers=n_layers, force_backend=force)
         out, lse = st.new_outputs()
         with no_gc_pauses():
