@@ -262,8 +262,14 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   // each short request's tiles go to a partial row set of its own, after
   // the suffix parts' rows
   for (int32_t r = inline_rank0; r < batch; ++r) a.ranks[r].part0 = static_cast<int32_t>(parts) + (r - inline_rank0);
-  a.join_blocks = a.need_merge ? inline_rank0 * n_kv + (batch - inline_rank0) : 0;
-  plan.n_short = batch - inline_rank0;
+  // short requests: one join workgroup each, or several when there are more
+  // of them than workgroup slots (a second round of workgroups would start
+  // only as the first round ends)
+  const int32_t n_short = batch - inline_rank0;
+  const int32_t short_per = n_short > step_slots ? static_cast<int32_t>(ceil_div(n_short, step_slots)) : 1;
+  a.short_per_block = short_per;
+  a.join_blocks = a.need_merge ? inline_rank0 * n_kv + static_cast<int32_t>(ceil_div(n_short, short_per)) : 0;
+  plan.n_short = n_short;
   plan.n_parts = static_cast<int32_t>(parts);
   plan.part_tokens = kSuffixPart;
   plan.suffix_blocks = a.suffix_blocks;

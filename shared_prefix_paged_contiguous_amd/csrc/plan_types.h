@@ -106,7 +106,9 @@ constexpr int kInlineTokens = 32;
 //
 // Grid: prefix blocks, then suffix blocks, then the joins: one per (ranked
 // request, KV head) for the requests ranked before inline_rank0, shortest
-// slot table first, then one per short request.  Prefix and suffix blocks
+// slot table first, then one per short request (or per short_per_block
+// consecutive short requests, when there are more of them than workgroup
+// slots).  Prefix and suffix blocks
 // never wait, and every join block follows all of them in each XCD's
 // (in-order) dispatch, so the joins' waits end.  The prefix and suffix
 // ranges of the grid are padded to 4 * xcds blocks.
@@ -142,7 +144,7 @@ struct StepHead {
   int32_t fold;                // suffix block i runs parts n_parts-1-i/n_kv and i/n_kv (see above)
   int32_t partial_f32;         // partial rows are fp32 (else the input dtype)
   int32_t inline_rank0;        // ranks [inline_rank0, batch) are short requests (no suffix part)
-  int32_t pad1_;
+  int32_t short_per_block;     // short requests per join workgroup (consecutive ranks)
   const void* q;
   void* out;
   float* lse;

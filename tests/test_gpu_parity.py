@@ -184,8 +184,15 @@ def test_largest_batch_parity(force):
     s = spec(n_q=8, n_kv=2, head_dim=64, batch=1024, prefix_len=200, hot_capacity=256, suffix_lo=0,
              suffix_hi=8, cold_capacity=16384)
     w = workloads.make(s)
-    _, out, lse, _ = run(w, force=force)
+    st, out, lse, _ = run(w, force=force)
     check(out, lse, *oracle_ref(w))
+    # every request is short; more of them than workgroup slots (two per CU):
+    # each join workgroup takes several consecutive ones
+    plan = st.ctx.last_plan()
+    slots = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    per = -(-1024 // slots)
+    assert plan["n_short_requests"] == 1024 and plan["n_suffix_blocks"] == 0
+    assert plan["n_join_blocks"] == -(-1024 // per)
 
 
 @pytest.mark.parametrize("batch", [127, 128, 129])
