@@ -366,7 +366,8 @@ typedef struct {
                                  many fit */
   int32_t n_join_blocks;      /* join workgroups (when some output is joined from several
                                  partials: one per request and KV head, but one per short
-                                 request; else 0) */
+                                 request, or per k consecutive short requests when they
+                                 outnumber the workgroup slots; else 0) */
   int32_t n_short_requests;   /* short requests: a HOT prefix and at most 32 slot-table tokens.
                                  They get no suffix part; one join workgroup per request
                                  attends each KV head's slot-table tile itself and joins it
@@ -377,6 +378,18 @@ typedef struct {
                                  kernel launch (the call returns right after the launch) */
 } gkv_plan_info;
 int gkv_last_plan(const gkv_ctx* ctx, gkv_plan_info* out);
+
+/* Plans a step without running it: the request grouping, backend rule and
+ * work decomposition that gkv_attn_decode / gkv_decode_step would use for
+ * these requests (hot_prefix_ids and cold_indptr_h as there; same shape
+ * checks), written to *out (workspace_bytes: what the bound workspace must
+ * hold; host_call_us 0).  Host only: no launch and no device memory access
+ * (the device's compute-unit count is read when a device is present; without
+ * one, gfx950's 256).  The plan is the same as the step's for the same
+ * arguments, context settings (gkv_set_dispatch) and pools.  Errors: those
+ * of gkv_attn_decode's host checks on these arguments. */
+int gkv_plan_step(gkv_ctx* ctx, int32_t batch, const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
+                  gkv_plan_info* out);
 
 /* Status of the steps run on the bound workspace since it was bound or last
  * read: *joins_timed_out = the number of (request, KV head) joins that gave

@@ -114,6 +114,7 @@ SIGNATURES = {
     "gkv_select_backend": (ctypes.c_int, [_P, _I32, _PI32]),
     "gkv_set_dispatch": (ctypes.c_int, [_P, _I32, _I32]),
     "gkv_last_plan": (ctypes.c_int, [_P, ctypes.POINTER(_PlanInfo)]),
+    "gkv_plan_step": (ctypes.c_int, [_P, _I32, _PI32, _PI32, ctypes.POINTER(_PlanInfo)]),
     "gkv_step_status": (ctypes.c_int, [_P, _P, _PI32]),
     "gkv_stream_read": (ctypes.c_int, [_P, ctypes.c_size_t, _I32, _P, _P]),
     "gkv_step_trace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
@@ -407,6 +408,17 @@ class Context:
     def last_plan(self) -> dict:
         p = _PlanInfo()
         self._check(self._lib.gkv_last_plan(self._h, ctypes.byref(p)), "last_plan")
+        return {f: getattr(p, f) for f, _ in _PlanInfo._fields_ if f not in ("pad_", "reserved")}
+
+    def plan_step(self, hot_prefix_ids, cold_indptr_h, batch: Optional[int] = None) -> dict:
+        """gkv_plan_step: the plan a step of these requests would use (host only)."""
+        ids = _i32(hot_prefix_ids)
+        ind = _i32(cold_indptr_h)
+        if batch is None:
+            batch = len(ids)
+        p = _PlanInfo()
+        self._check(self._lib.gkv_plan_step(self._h, batch, ids.ctypes.data_as(_PI32), ind.ctypes.data_as(_PI32),
+                                            ctypes.byref(p)), "plan_step")
         return {f: getattr(p, f) for f, _ in _PlanInfo._fields_ if f not in ("pad_", "reserved")}
 
 

@@ -546,6 +546,57 @@ int read_topology(gkv_ctx* ctx) {
   return GKV_OK;
 }
 
+// Workspace layout of a planned step: [counters][status][prefix o][prefix
+// lse][suffix o][suffix lse]; in the static scratch: [status][counters (room
+// for any context)][the same partials].
+struct StepLayout {
+  size_t off_po, off_pl, off_so, off_sl, need;
+};
+StepLayout step_layout(const gkv_config& c, const gkv::Plan& plan, bool use_static) {
+  const size_t row = static_cast<size_t>(c.head_dim) * partial_size(c);
+  StepLayout l;
+  l.off_po = use_static ? gkv::kStaticControlBytes : control_bytes(c);
+  l.off_pl = l.off_po + gkv::align256(plan.prefix_rows * row);
+  l.off_so = l.off_pl + gkv::align256(plan.prefix_rows * 4);
+  l.off_sl = l.off_so + gkv::align256(plan.suffix_rows * row);
+  l.need = l.off_sl + gkv::align256(plan.suffix_rows * 4);
+  return l;
+}
+
+// The backend of a step of `batch` requests (the rule, or the forced one);
+// dense with fp32 elements falls back to cascade unless forced (an error).
+int step_backend(gkv_ctx* ctx, int32_t batch, int32_t* backend) {
+  const gkv_config& c = ctx->cfg;
+  *backend = gkv::choose_backend(batch, c.n_q_heads / c.n_kv_heads, ctx->m_sat, ctx->force);
+  if (*backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) {
+    if (ctx->force == GKV_BACKEND_DENSE) return fail(ctx, GKV_ERR_INVALID, "the dense backend is bf16 only");
+    *backend = GKV_BACKEND_CASCADE;
+  }
+  return GKV_OK;
+}
+
+gkv::PlanShape plan_shape(const gkv_ctx* ctx) {
+  gkv::PlanShape shape = shape_of(ctx->cfg);
+  shape.xcds = ctx->dev_xcds;
+  shape.cus = ctx->dev_cus;
+  return shape;
+}
+
+void fill_info(gkv_plan_info& i, const gkv::Plan& plan, int32_t backend, size_t need) {
+  i.backend = backend;
+  i.m_eff = plan.m_eff;
+  i.n_classes = plan.n_classes;
+  i.n_prefix_blocks = plan.prefix_blocks;
+  i.n_suffix_blocks = plan.suffix_blocks;
+  i.n_suffix_parts = plan.n_parts;
+  i.joins_partials = plan.multi_part;
+  i.suffix_part_tokens = plan.part_tokens;
+  i.folded_parts = plan.fold;
+  i.n_join_blocks = plan.join_blocks;
+  i.n_short_requests = plan.n_short;
+  i.workspace_bytes = static_cast<int64_t>(need);
+}
+
 // The decode step behind gkv_attn_decode (k_new == nullptr), gkv_decode_step
 // (the batch's new tokens appended inside the launch) and
 // gkv_decode_step_static (the same, its scratch in the library's static
@@ -579,29 +630,18 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
                                               " has an empty slot table (its new token must be its last entry)");
   }
 
-  int32_t backend = gkv::choose_backend(batch, group, ctx->m_sat, ctx->force);
-  if (backend == GKV_BACKEND_DENSE && c.dtype != GKV_BF16) {
-    if (ctx->force == GKV_BACKEND_DENSE) return fail(ctx, GKV_ERR_INVALID, "the dense backend is bf16 only");
-    backend = GKV_BACKEND_CASCADE;
-  }
+  int32_t backend = 0;
+  if (int r = step_backend(ctx, batch, &backend)) return r;
 
   gkv::Plan plan;
   std::string err;
   gkv::StepArgs& a = ctx->args;
-  gkv::PlanShape shape = shape_of(c);
-  shape.xcds = ctx->dev_xcds;
-  shape.cus = ctx->dev_cus;
-  if (gkv::build_plan(shape, ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
+  if (gkv::build_plan(plan_shape(ctx), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, a, plan, err) != 0)
     return fail(ctx, GKV_ERR_INVALID, err);
 
-  // workspace: [counters][status][prefix o][prefix lse][suffix o][suffix lse];
-  // static scratch: [status][counters (room for any context)][the same partials]
-  const size_t row = static_cast<size_t>(c.head_dim) * partial_size(c);
-  const size_t off_po = use_static ? gkv::kStaticControlBytes : control_bytes(c);
-  const size_t off_pl = off_po + gkv::align256(plan.prefix_rows * row);
-  const size_t off_so = off_pl + gkv::align256(plan.prefix_rows * 4);
-  const size_t off_sl = off_so + gkv::align256(plan.suffix_rows * row);
-  const size_t need = off_sl + gkv::align256(plan.suffix_rows * 4);
+  const StepLayout lay = step_layout(c, plan, use_static);
+  const size_t off_po = lay.off_po, off_pl = lay.off_pl, off_so = lay.off_so, off_sl = lay.off_sl;
+  const size_t need = lay.need;
   if (use_static && need > gkv::kStaticScratchBytes)
     return fail(ctx, GKV_ERR_INVALID, "step needs " + std::to_string(need) + " bytes of scratch; the static "
                                       "scratch of gkv_decode_step_static holds " +
@@ -675,18 +715,7 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
   if ((e = gkv::launch_step(a, c.dtype, backend, st, ev)) != hipSuccess) return device_fail(ctx, "step launch", e);
   const auto t_launched = std::chrono::steady_clock::now();
 
-  ctx->last.backend = backend;
-  ctx->last.m_eff = plan.m_eff;
-  ctx->last.n_classes = plan.n_classes;
-  ctx->last.n_prefix_blocks = plan.prefix_blocks;
-  ctx->last.n_suffix_blocks = plan.suffix_blocks;
-  ctx->last.n_suffix_parts = plan.n_parts;
-  ctx->last.joins_partials = plan.multi_part;
-  ctx->last.suffix_part_tokens = plan.part_tokens;
-  ctx->last.folded_parts = plan.fold;
-  ctx->last.n_join_blocks = plan.join_blocks;
-  ctx->last.n_short_requests = plan.n_short;
-  ctx->last.workspace_bytes = static_cast<int64_t>(need);
+  fill_info(ctx->last, plan, backend, need);
   ctx->last.host_plan_us = std::chrono::duration<double, std::micro>(t_planned - t_start).count();
   ctx->last.host_call_us = std::chrono::duration<double, std::micro>(t_launched - t_start).count();
   ctx->have_last = true;
@@ -697,6 +726,28 @@ int decode_impl(gkv_ctx* ctx, int32_t layer, const void* q, const void* k_new, c
 }  // namespace
 
 extern "C" {
+
+int gkv_plan_step(gkv_ctx* ctx, int32_t batch, const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,
+                  gkv_plan_info* out) {
+  if (!ctx || !out) return GKV_ERR_INVALID;
+  const auto t_start = std::chrono::steady_clock::now();
+  if (int r = read_topology(ctx)) return r;
+  if (batch < 1) return fail(ctx, GKV_ERR_INVALID, "batch must be >= 1");
+  if (!hot_prefix_ids || !cold_indptr_h) return fail(ctx, GKV_ERR_INVALID, "plan_step: null pointer argument");
+  int32_t backend = 0;
+  if (int r = step_backend(ctx, batch, &backend)) return r;
+  gkv::Plan plan;
+  std::string err;
+  if (gkv::build_plan(plan_shape(ctx), ctx->hot, batch, hot_prefix_ids, cold_indptr_h, backend, ctx->args, plan,
+                      err) != 0)
+    return fail(ctx, GKV_ERR_INVALID, err);
+  gkv_plan_info info{};
+  fill_info(info, plan, backend, step_layout(ctx->cfg, plan, false).need);
+  info.host_plan_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t_start).count();
+  info.host_call_us = 0.0;
+  *out = info;
+  return GKV_OK;
+}
 
 int gkv_attn_decode(gkv_ctx* ctx, int32_t layer, const void* q, int32_t batch,
                     const int32_t* hot_prefix_ids, const int32_t* cold_indptr_h,

@@ -279,3 +279,73 @@ def test_step_rejects_more_than_64_hot_classes_before_any_device_work():
     indptr = list(range(66))
     with pytest.raises(binding.GkvError, match="more than 64 distinct HOT prefixes"):
         c.attn_decode(0, 16, ids, indptr, 16, 16, 16, 16, batch=65, stream=0)
+
+
+# ------------------------------------------------------------------ planner
+# gkv_plan_step runs the step's planner alone (host only).  Without a GPU it
+# plans for gfx950's 256 compute units in 8 XCDs: 512 workgroup slots (two per
+# CU), grid ranges padded to 32 workgroups.
+def _llama_ctx(hot=16384, cold=1 << 20):
+    return _ctx(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16", hot_capacity_tokens=hot,
+                cold_capacity_tokens=cold)
+
+
+def test_plan_of_the_bench_step():
+    """Llama-3.1-8B shape, one 16K HOT prefix, 64 requests of 128..1024 suffix
+    tokens: cascade (M_eff 256 < 4096); 16K tokens x 8 KV heads x 2 M-tiles
+    of 32 requests = 262144 units over 256 target workgroups gives 1024-token
+    splits, 16 per (KV head, M-tile): 256 prefix workgroups.  64 parts x 8 KV
+    heads = 512 workgroups overflow the 256 slots left, 32 folded pairs x 8 =
+    256 fit: folded.  One join per (request, KV head): 512."""
+    c = _llama_ctx()
+    pid, _ = c.hot_pool_alloc(16384)
+    lens = np.random.default_rng(5).integers(128, 1025, size=64)
+    indptr = np.concatenate([[0], np.cumsum(lens)])
+    p = c.plan_step([pid] * 64, indptr)
+    assert p["backend"] == binding.BACKEND_CASCADE and p["m_eff"] == 256 and p["n_classes"] == 1
+    assert (p["n_prefix_blocks"], p["n_suffix_blocks"], p["n_join_blocks"]) == (256, 256, 512)
+    assert p["folded_parts"] == 1 and p["n_suffix_parts"] == 64 and p["n_short_requests"] == 0
+    assert p["joins_partials"] == 1 and p["workspace_bytes"] > 0
+    # the grid does not depend on the order the requests come in
+    q = c.plan_step([pid] * 64, np.concatenate([[0], np.cumsum(lens[::-1])]))
+    assert {k: v for k, v in q.items() if not k.startswith("host")} == {k: v for k, v in p.items() if not k.startswith("host")}
+
+
+@pytest.mark.parametrize("batch,joins", [(256, 256), (512, 512), (513, 257), (1024, 512)])
+def test_plan_groups_short_requests_beyond_the_slots(batch, joins):
+    """One-token requests on a HOT prefix are short requests: no suffix part,
+    one join workgroup each, or k = ceil(n / 512) consecutive ones per join
+    workgroup when there are more than the 512 slots."""
+    c = _llama_ctx(hot=2048)
+    pid, _ = c.hot_pool_alloc(2048)
+    p = c.plan_step([pid] * batch, np.arange(batch + 1))
+    assert p["n_short_requests"] == batch and p["n_suffix_parts"] == 0 and p["n_suffix_blocks"] == 0
+    assert p["n_join_blocks"] == joins
+
+
+def test_plan_dense_split_rule():
+    """Forced dense, 1024 one-token requests on a 16K prefix: 32 M-tiles x 8 KV
+    heads = 256 (M-tile, head) pairs.  The rule's time, with k = ceil(blocks /
+    256 CUs) workgroups per CU of one split each (two at a time 1.25x as fast,
+    plus eight blocks' fixed cost): 1 split 16384 + 256 = 16640; 2 splits
+    (k = 2) 2 x 8448 / 1.25 = 13517; 3 (k = 3) 2 x 5718 / 1.25 + 5718 = 14867;
+    4 (k = 4) 4 x 4352 / 1.25 = 13926: two splits, 512 prefix workgroups."""
+    c = _llama_ctx()
+    pid, _ = c.hot_pool_alloc(16384)
+    c.set_dispatch(binding.BACKEND_DENSE)
+    p = c.plan_step([pid] * 1024, np.arange(1025))
+    assert p["backend"] == binding.BACKEND_DENSE and p["m_eff"] == 4096
+    assert p["n_prefix_blocks"] == 512 and p["n_join_blocks"] == 512 and p["n_suffix_blocks"] == 0
+
+
+def test_plan_step_checks_like_the_step():
+    c = _llama_ctx()
+    pid, _ = c.hot_pool_alloc(100)
+    with pytest.raises(binding.GkvError, match="not live"):
+        c.plan_step([pid + 3], [0, 1])
+    with pytest.raises(binding.GkvError, match="decreases"):
+        c.plan_step([pid, pid], [0, 2, 1])
+    with pytest.raises(binding.GkvError, match="exceeds the per-call limit"):
+        c.plan_step([pid] * 1025, np.arange(1026))
+    with pytest.raises(binding.GkvError, match="batch"):
+        c.plan_step([], [0], batch=0)

@@ -209,6 +209,11 @@ def test_argument_forms_at_their_edge(batch, force):
     st, out, lse, backend = run(w, force=force)
     assert backend == force
     check(out, lse, *oracle_ref(w))
+    # gkv_plan_step gives the plan of the step that ran
+    ran = st.ctx.last_plan()
+    planned = st.ctx.plan_step(st.hot_ids, st.indptr_h)
+    assert {k: v for k, v in planned.items() if not k.startswith("host")} == \
+        {k: v for k, v in ran.items() if not k.startswith("host")}
 
 
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
