@@ -369,9 +369,9 @@ typedef struct {
                                  request, or per k consecutive short requests when they
                                  outnumber the workgroup slots; else 0) */
   int32_t n_short_requests;   /* short requests: a HOT prefix and at most 32 slot-table tokens.
-                                 They get no suffix part; one join workgroup per request
-                                 attends each KV head's slot-table tile itself and joins it
-                                 with the prefix splits */
+                                 They get no suffix part; their join workgroup (one per
+                                 request, or per k requests) attends each KV head's
+                                 slot-table tile itself and joins it with the prefix splits */
   int64_t workspace_bytes;    /* workspace bytes the step used */
   double host_plan_us;        /* host time spent validating and planning */
   double host_call_us;        /* host time of the whole call: validation, planning and the

@@ -1824,8 +1824,8 @@ __device__ __forceinline__ void short_join(const A& a, int r0, int nr, int blk) 
 // ranks taken shortest slot table first (their partials arrive first): waits
 // for the arrival of all partials, then wave w joins the request's query
 // heads g*G + w, g*G + w + 4, ...  Where the partials lie is read before the
-// wait, so after it only the partials themselves are loaded.  The rest: one
-// short request each.
+// wait, so after it only the partials themselves are loaded.  The rest:
+// short_per_block consecutive short requests each (the last: what remains).
 template <typename T, int D, typename P, class A>
 __device__ __forceinline__ void join_block(const A& a, int j) {
   const int blk = a.prefix_blocks + a.suffix_blocks + j;

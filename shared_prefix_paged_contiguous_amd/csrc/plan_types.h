@@ -95,13 +95,15 @@ struct ClassDesc {
 //
 // Short requests: a request with a HOT prefix whose slot table holds at
 // most kInlineTokens tokens (one tile) gets no suffix part.  Ranked after all
-// other requests, it has one join workgroup of its own that attends every KV
-// head's slot-table tile itself (wave w takes KV heads w, w + 4, ...) into a
-// partial row set of its own (rows after the suffix parts'; ranks[r].part0
-// names it), waits once for the prefix splits of all its KV heads and joins
-// them.  Steps whose requests carry a token or a few each (prefix-bound
-// steps) thus launch one workgroup per request, instead of two per
-// (request, KV head), and its tiles overlap the prefix when slots are free.
+// other requests, it has a join workgroup (its own, or shared with the next
+// short requests when they outnumber the workgroup slots) that attends every
+// KV head's slot-table tile itself (wave w takes KV heads w, w + 4, ...)
+// into a partial row set of its own (rows after the suffix parts';
+// ranks[r].part0 names it), waits once for the prefix splits of all its KV
+// heads and joins them.  Steps whose requests carry a token or a few each
+// (prefix-bound steps) thus launch one workgroup per request or fewer,
+// instead of two per (request, KV head), and the tiles overlap the prefix
+// when slots are free.
 constexpr int kInlineTokens = 32;
 //
 // Grid: prefix blocks, then suffix blocks, then the joins: one per (ranked
