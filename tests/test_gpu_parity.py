@@ -284,6 +284,23 @@ def test_short_requests_join_their_own_tiles(n_q, n_kv, d, dtype, force):
     check(out, lse, *oracle_ref(w), **(FP32_TOL if dtype == "f32" else {}))
 
 
+@pytest.mark.parametrize("prefix_len", [1000, 2048, 4096])
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_short_request_joins_by_partial_count(prefix_len, force):
+    """Short requests of the Llama-3.1-8B attention shape whose joins take
+    each of their three forms: at most 8 partials (1000-token prefix), 9
+    (2048: 8 prefix splits and the request's tile) and 17 (4096: 16 splits);
+    tables of 0..32 tokens, so some requests have no tile of their own."""
+    lens = tuple((i * 7) % 33 for i in range(64))
+    s = spec(batch=64, prefix_len=prefix_len, hot_capacity=-(-prefix_len // 32) * 32, cold_capacity=4096,
+             fixed_suffix=lens)
+    w = workloads.make(s)
+    st, out, lse, backend = run(w, force=force)
+    assert backend == force and st.ctx.last_plan()["n_short_requests"] == 64
+    check(out, lse, *oracle_ref(w))
+    assert st.ctx.step_status() == 0
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_prefix_bound_step_of_short_requests(force):
     """A prefix-bound step: 256 requests of the Llama-3.1-8B attention shape
