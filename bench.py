@@ -857,8 +857,8 @@ def main():
     ap.add_argument("--fit-batches", default="8,16,32,64,128,256,384,512,768")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step shards by "
-              "KV head with no exchange inside attention; see DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (a decode step would shard "
+              "by KV head, with no exchange inside attention). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     import torch

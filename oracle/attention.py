@@ -9,7 +9,7 @@ context "prefix tokens, then suffix tokens".  This module writes that plain
 definition out; it does not split or merge anything (``merge`` exists only so
 tests can check the invariant).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * scale 1/sqrt(d);
 * grouped-query attention maps query head h to KV head floor(h / G) with
   G = n_q / n_kv (contiguous groups);
