@@ -439,21 +439,74 @@ __device__ __forceinline__ void softmax_ref(ColState<T, D> (&st)[RB], f32x4 (&s0
     }
   }
 }
-// Probabilities of one block against the current reference points, and the
-// lanes' shares of the row sums.
-template <typename T, int D, int RB>
-__device__ __forceinline__ void softmax_p(ColState<T, D> (&st)[RB], const f32x4 (&s0)[RB], const f32x4 (&s1)[RB], float c,
-                                          f32x4 (&p0)[RB], f32x4 (&p1)[RB]) {
+// The pipelined prefix loop keeps a block's scores as y = s*c - m, formed
+// when the block's QK^T product is done (beside the PV products of the block
+// before), so that the weights exp2(y) cost the VALU no scale and subtract
+// beside the next QK^T products.  softmax_ref_y masks tokens >= valid, forms
+// y against the current reference points and moves them lazily (a column's y
+// above kLazy: rare), shifting the state and this block's y with them; the
+// reference points must be set (the first block of a split goes through
+// softmax_ref and shift_scores).
+template <int RB>
+__device__ __forceinline__ void shift_scores(f32x4 (&s0)[RB], f32x4 (&s1)[RB], const float (&m)[RB], float c) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    ColState<T, D>& cs = st[rb];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p0[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[rb][i], c, -cs.m));
-      p1[rb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[rb][i], c, -cs.m));
+      s0[rb][i] = __builtin_fmaf(s0[rb][i], c, -m[rb]);
+      s1[rb][i] = __builtin_fmaf(s1[rb][i], c, -m[rb]);
     }
-    cs.add_sum(p0[rb], p1[rb]);
+}
+template <typename T, int D, int RB>
+__device__ __forceinline__ void softmax_ref_y(ColState<T, D> (&st)[RB], f32x4 (&s0)[RB], f32x4 (&s1)[RB], int valid,
+                                              int g, float c) {
+  if (valid < 32) {
+    int v = __builtin_amdgcn_readfirstlane(valid);
+    asm volatile("" : "+s"(v));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * g + i >= v) s0[rb][i] = kNegInf;
+        if (16 + 4 * g + i >= v) s1[rb][i] = kNegInf;
+      }
   }
+  float m[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) m[rb] = st[rb].m;
+  shift_scores<RB>(s0, s1, m, c);
+  float lmx[RB];
+  bool jump = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    lmx[rb] = fmaxf(fmaxf(fmaxf(s0[rb][0], s0[rb][1]), fmaxf(s0[rb][2], s0[rb][3])),
+                    fmaxf(fmaxf(s1[rb][0], s1[rb][1]), fmaxf(s1[rb][2], s1[rb][3])));
+    jump = jump || lmx[rb] > kLazy;
+  }
+  if (__any(jump)) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ColState<T, D>& cs = st[rb];
+      const float d = fmaxf(wave_max_groups(lmx[rb]), 0.f);
+      cs.rescale(__builtin_amdgcn_exp2f(-d));
+      cs.m += d;
+      s0[rb] -= d;
+      s1[rb] -= d;
+    }
+  }
+}
+// Weights exp2(y) of one block (no row sums: those go beside the PV
+// products).
+template <int RB>
+__device__ __forceinline__ void softmax_py(const f32x4 (&y0)[RB], const f32x4 (&y1)[RB], f32x4 (&p0)[RB],
+                                           f32x4 (&p1)[RB]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0[rb][i] = __builtin_amdgcn_exp2f(y0[rb][i]);
+      p1[rb][i] = __builtin_amdgcn_exp2f(y1[rb][i]);
+    }
 }
 
 // Partials cross workgroups (and XCDs, whose L2 caches are not coherent
@@ -1489,16 +1542,18 @@ __device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_
 
   if constexpr (kPipeK) {
     // Software pipeline over blocks.  S(i) = QK^T of block i is computed in
-    // iteration i - 1, and its reference points are moved right after (rare
-    // branch).  Iteration i waits for block i + 1 and passes the barrier
-    // (block i - 1's slot is then free: its K was read in iteration i - 2,
-    // its V in i - 1), issues the copy of block i + kStages - 1, reads K(i+1)
-    // and V(i), then runs one branch-free region: the QK^T of block i + 1 on
-    // the matrix cores interleaved with the softmax of S(i) on the VALU, then
-    // PV(i); last, the reference points for S(i + 1).  Only the last block
-    // can be partial; it is masked when its scores are formed and done after
-    // the loop.  The loop is unrolled by two so that the score tiles of
-    // consecutive blocks alternate between two register sets (no copies).
+    // iteration i - 1, then shifted to y = s*c - m with its reference points
+    // moved (rare branch).  Iteration i waits for block i + 1 and passes the
+    // barrier (block i - 1's slot is then free: its K was read in iteration
+    // i - 2, its V in i - 1), issues the copy of block i + kStages - 1, reads
+    // K(i+1) and V(i), then runs one branch-free region: the QK^T of block
+    // i + 1 on the matrix cores interleaved with the weights exp2(y(i)) on
+    // the VALU, then PV(i) beside the row sums; last, the shift of S(i + 1)
+    // (the scale and subtract out of the exp2 region: 1-2% on dense steps).
+    // Only the last block can be partial; it is masked when its scores are
+    // formed and done after the loop.  The loop is unrolled by two so that
+    // the score tiles of consecutive blocks alternate between two register
+    // sets (no copies).
     auto valid_of = [&](int j) { return min(kHotBlock, t1 - t0 - kHotBlock * j); };
     f32x4 s0[RB], s1[RB], n0[RB], n1[RB];
     wait_block(0, min(nb - 1, kStages - 2));
@@ -1507,6 +1562,10 @@ __device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_
       read_k(k, 0);
       qk_rows<T, D, RB>(st, k.k0, k.k1, s0, s1);
       softmax_ref<T, D, RB>(st, s0, s1, valid_of(0), g, c);
+      float m[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) m[rb] = st[rb].m;
+      shift_scores<RB>(s0, s1, m, c);
     }
     // iteration i: S(i) in (c0, c1), S(i + 1) into (x0, x1)
     auto iteration = [&](int i, f32x4 (&c0)[RB], f32x4 (&c1)[RB], f32x4 (&x0)[RB], f32x4 (&x1)[RB]) {
@@ -1519,20 +1578,24 @@ __device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_
         read_v(vo, i);
         f32x4 p0[RB], p1[RB];
         qk_rows<T, D, RB>(st, k.k0, k.k1, x0, x1);
-        softmax_p<T, D, RB>(st, c0, c1, c, p0, p1);
+        softmax_py<RB>(c0, c1, p0, p1);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
-        // 16 VALU instructions of the softmax first (the first QK^T(i + 1)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) st[rb].add_sum(p0[rb], p1[rb]);
+        // kLead VALU instructions of the weights first (the first QK^T(i + 1)
         // product waits for K(i + 1) from LDS, and issue is in order: work
         // placed behind it would wait too), then one MFMA of QK^T(i + 1) and
-        // two VALU instructions, repeated; the PV products follow
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        // one VALU instruction (the exp2 are quarter rate), repeated; the PV
+        // products follow, beside the row sums and the shift of S(i + 1)
+        constexpr int kLead = 8;
+        __builtin_amdgcn_sched_group_barrier(0x002, kLead, 0);
 #pragma unroll
         for (int x = 0; x < 2 * RB * TR::KS; ++x) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
         }
-        softmax_ref<T, D, RB>(st, x0, x1, valid_of(i + 1), g, c);
+        softmax_ref_y<T, D, RB>(st, x0, x1, valid_of(i + 1), g, c);
       }
     };
     int i = 0;
@@ -1559,9 +1622,12 @@ __device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_
         TR::mask_v(vo, v, g);
       }
       f32x4 p0[RB], p1[RB];
-      softmax_p<T, D, RB>(st, s0, s1, c, p0, p1);
+      softmax_py<RB>(s0, s1, p0, p1);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
+      for (int rb = 0; rb < RB; ++rb) {
+        st[rb].add_sum(p0[rb], p1[rb]);
+        TR::pv(st[rb].acc, vo, p0[rb], p1[rb]);
+      }
     }
   } else {
     for (int i = 0; i < nb; ++i) {
