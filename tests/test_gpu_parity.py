@@ -176,6 +176,55 @@ def test_fp32_head_dims(d):
     check(out, lse, *oracle_ref(w), **FP32_TOL)
 
 
+def _spike(w, rows, toks, b, h, lam):
+    """Sets key rows toks of `rows` ([tokens, n_kv, d]) for KV head h // G to
+    lam * q[b, h] / |q[b, h]|: that query's score there is about lam."""
+    G = w.spec.n_q // w.spec.n_kv
+    q = w.q[b, h].float()
+    k = (lam * q / q.norm()).to(rows.dtype)
+    for t in toks:
+        rows[t, h // G] = k
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("force", [CASCADE, DENSE])
+def test_score_jumps_move_the_reference_points(dtype, force):
+    """Scores that jump far above the running maximum in the middle of a
+    prefix split, in its last partial block and inside suffix parts, and
+    queries whose scores climb block after block: the lazily moved reference
+    points of the online softmax (a move is rare with N(0,1) data) against
+    the oracle."""
+    if dtype == "f32" and force == DENSE:
+        pytest.skip("fp32 runs the cascade backend only")
+    s = spec(n_q=8, n_kv=2, head_dim=128, dtype=dtype, batch=6, prefix_len=3000, hot_capacity=3008,
+             fixed_suffix=(0, 40, 300, 900, 33, 2000))
+    w = workloads.make(s)
+    pk = w.prefix_k[0]
+    # upward jumps mid-split (split lengths are multiples of 64 tokens), in the
+    # last partial block, and late in a long range
+    _spike(w, pk, [100, 700], b=0, h=1, lam=30.0)
+    _spike(w, pk, [2990], b=1, h=4, lam=60.0)
+    _spike(w, pk, [1500, 1501], b=2, h=7, lam=15.0)
+    # queries scaled up: their scores spread over tens of units, so the
+    # running maximum climbs by more than the lazy threshold again and again
+    # over the blocks of every split
+    w.q[4, 3] = (w.q[4, 3].float() * 8.0).to(w.q.dtype)
+    w.q[5, 6] = (w.q[5, 6].float() * 10.0).to(w.q.dtype)
+    # suffix parts: a jump mid-part and one on the last (current) token
+    for b, toks in ((3, [500]), (5, [10, 1999]), (4, [32])):
+        lo = int(w.suffix_offsets[b])
+        sk = w.suffix_k[lo:int(w.suffix_offsets[b + 1])]
+        _spike(w, sk, toks, b=b, h=2 * b % w.spec.n_q, lam=40.0)
+    _, out, lse, backend = run(w, force=force)
+    assert backend == force
+    ref_o, ref_l = oracle_ref(w)
+    assert float(np.abs(ref_l).max()) > 20.0   # the jumps are in the reference
+    if dtype == "f32":
+        check(out, lse, ref_o, ref_l, **FP32_TOL)
+    else:
+        check(out, lse, ref_o, ref_l)
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_largest_batch_parity(force):
     """The largest batch one step takes (1024 requests): one shared prefix,
