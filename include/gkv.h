@@ -365,9 +365,12 @@ typedef struct {
                                  overflow the workgroup slots beside the prefix while half as
                                  many fit */
   int32_t n_join_blocks;      /* join workgroups (when some output is joined from several
-                                 partials: one per request and KV head, but one per short
-                                 request, or per k consecutive short requests when they
-                                 outnumber the workgroup slots; else 0) */
+                                 partials: one per request and KV head when some slot table
+                                 spans several suffix parts, none for the others when every
+                                 table is one part (the suffix workgroups then join their
+                                 requests themselves); one per short request, or per k
+                                 consecutive short requests when they outnumber the
+                                 workgroup slots; else 0) */
   int32_t n_short_requests;   /* short requests: a HOT prefix and at most 32 slot-table tokens.
                                  They get no suffix part; their join workgroup (one per
                                  request, or per k requests) attends each KV head's

@@ -810,6 +810,180 @@ __device__ __forceinline__ void join_row(const A& a, const JoinSrc& src, int b, 
     a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
 }
 
+// One wave joins request b's ns prefix partials for query head h with NL
+// partials held in LDS (a suffix part joined in the workgroup that attended
+// it: row p at loc_o + p * o_stride, D fp32 values, base-2 lse at
+// loc_lse[p * l_stride]) and writes out[b][h] and lse[b][h].  Same
+// arithmetic and load pattern as join_row; the LDS partials enter the
+// reference point from the start and their weighted rows are added by lane
+// group 0 before the cross-lane sum.
+template <typename T, int D, typename P, int NL_LOC, class A>
+__device__ __forceinline__ void join_local(const A& a, int ns, int b, int h, const float* loc_o, int o_stride,
+                                           const float* loc_lse, int l_stride, int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;   // 16-byte chunks per partial row
+  constexpr int RPI = 64 / CH;                                 // rows per wave-wide access
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));      // values per chunk
+  constexpr int NB = 32;                                       // partials per batch
+  constexpr int NL = NB / RPI;                                 // chunk loads per lane per batch
+  static_assert(CH <= 64 && 64 % CH == 0, "row chunks must tile the wave");
+  const int ch = lane % CH, rg = lane / CH;
+  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
+  auto lse_of = [&](int p) { return load_partial(a.p_lse + prow0 + static_cast<size_t>(p) * a.n_q); };
+  auto chunk_of = [&](int p) {
+    return load_partial_chunk(static_cast<const P*>(a.p_o) + (prow0 + static_cast<size_t>(p) * a.n_q) * D + EPC * ch);
+  };
+  auto wave_max = [](float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+  };
+  float llse[NL_LOC];
+  float lmx = kNegInf;
+#pragma unroll
+  for (int p = 0; p < NL_LOC; ++p) {
+    llse[p] = loc_lse[p * l_stride];
+    lmx = fmaxf(lmx, llse[p]);
+  }
+  float mx = lmx;
+  if (ns > NB) {
+    float x = kNegInf;
+    for (int base = 0; base < ns; base += 64) x = fmaxf(x, base + lane < ns ? lse_of(base + lane) : kNegInf);
+    mx = fmaxf(lmx, wave_max(x));
+  }
+  float acc[EPC];
+#pragma unroll
+  for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+  float wsum = 0.f;
+  for (int base = 0; base < ns; base += NB) {
+    const int cnt = min(NB, ns - base);
+    const float lp = lane < cnt ? lse_of(base + lane) : kNegInf;
+    u32x4 raw[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) raw[i] = chunk_of(base + min(i * RPI + rg, cnt - 1));
+    if (ns <= NB) mx = fmaxf(lmx, wave_max(lp));
+    const float wl = lane < cnt && lp != kNegInf ? __builtin_amdgcn_exp2f(lp - mx) : 0.f;
+    wsum += wl;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const float w = __shfl(wl, i * RPI + rg);   // zero for rows past cnt
+      float v[EPC];
+      unpack_chunk<P>(raw[i], v);
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] += w * v[j];
+    }
+  }
+  // the LDS partials (once: lane group 0; their weights join the sum once)
+  float wloc = 0.f;
+#pragma unroll
+  for (int p = 0; p < NL_LOC; ++p) {
+    const float w = llse[p] != kNegInf ? __builtin_amdgcn_exp2f(llse[p] - mx) : 0.f;
+    wloc += w;
+    if (rg == 0)
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] += w * loc_o[p * o_stride + EPC * ch + j];
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] += __shfl_xor(acc[j], off);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  wsum += wloc;
+  // no tokens in any part: an empty result, o = 0 and lse = -inf
+  const bool empty = !(wsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / wsum;
+  if (rg == 0) {
+    T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + EPC * ch;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) dst[k] = static_cast<T>(acc[k] * inv);
+  }
+  if (lane == 0)
+    a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
+}
+
+// join_local in two halves for up to 32 prefix partials, so that a wave can
+// issue the loads of two joins before it waits for either: local_loads issues
+// the lse and row-chunk loads, local_finish weighs them with the LDS
+// partials and writes the output (same arithmetic as join_local).
+template <int NL>
+struct LocalLoads {
+  float lp;
+  u32x4 raw[NL];
+};
+template <typename T, int D, typename P, class A>
+__device__ __forceinline__ LocalLoads<32 / (64 / (D * static_cast<int>(sizeof(P)) / 16))> local_loads(
+    const A& a, int ns, int b, int h, int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;
+  constexpr int RPI = 64 / CH;
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));
+  constexpr int NL = 32 / RPI;
+  const int ch = lane % CH, rg = lane / CH;
+  const size_t prow0 = static_cast<size_t>(b) * a.max_splits * a.n_q + h;
+  LocalLoads<NL> r;
+  r.lp = lane < ns ? load_partial(a.p_lse + prow0 + static_cast<size_t>(lane) * a.n_q) : kNegInf;
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    r.raw[i] = load_partial_chunk(static_cast<const P*>(a.p_o) +
+                                  (prow0 + static_cast<size_t>(min(i * RPI + rg, ns - 1)) * a.n_q) * D + EPC * ch);
+  return r;
+}
+template <typename T, int D, typename P, int NL_LOC, int NL, class A>
+__device__ __forceinline__ void local_finish(const A& a, const LocalLoads<NL>& r, int ns, int b, int h,
+                                             const float* loc_o, int o_stride, const float* loc_lse, int l_stride,
+                                             int lane) {
+  constexpr int CH = D * static_cast<int>(sizeof(P)) / 16;
+  constexpr int RPI = 64 / CH;
+  constexpr int EPC = 16 / static_cast<int>(sizeof(P));
+  const int ch = lane % CH, rg = lane / CH;
+  float llse[NL_LOC];
+  float mx = r.lp;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+#pragma unroll
+  for (int p = 0; p < NL_LOC; ++p) {
+    llse[p] = loc_lse[p * l_stride];
+    mx = fmaxf(mx, llse[p]);
+  }
+  const float wl = lane < ns && r.lp != kNegInf ? __builtin_amdgcn_exp2f(r.lp - mx) : 0.f;
+  float acc[EPC];
+#pragma unroll
+  for (int j = 0; j < EPC; ++j) acc[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const float w = __shfl(wl, i * RPI + rg);   // zero for rows past ns
+    float v[EPC];
+    unpack_chunk<P>(r.raw[i], v);
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] += w * v[j];
+  }
+  float wloc = 0.f;
+#pragma unroll
+  for (int p = 0; p < NL_LOC; ++p) {
+    const float w = llse[p] != kNegInf ? __builtin_amdgcn_exp2f(llse[p] - mx) : 0.f;
+    wloc += w;
+    if (rg == 0)
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) acc[j] += w * loc_o[p * o_stride + EPC * ch + j];
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1)
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) acc[j] += __shfl_xor(acc[j], off);
+  float wsum = wl;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off);
+  wsum += wloc;
+  const bool empty = !(wsum > 0.f);
+  const float inv = empty ? 0.f : 1.f / wsum;
+  if (rg == 0) {
+    T* dst = static_cast<T*>(a.out) + (static_cast<size_t>(b) * a.n_q + h) * D + EPC * ch;
+#pragma unroll
+    for (int k = 0; k < EPC; ++k) dst[k] = static_cast<T>(acc[k] * inv);
+  }
+  if (lane == 0)
+    a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
+}
+
 // Joins the partials of request b for the G query heads of KV head gk, 64 /
 // CH heads per pass: lane l takes 16-byte chunk l % CH of query head
 // gk * G + l / CH and walks the partials itself, NB at a time with all their
@@ -989,6 +1163,32 @@ __device__ __forceinline__ void wait_arrivals(const A& a, int b, int g, int n) {
   __hip_atomic_fetch_add(cnt, -n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// wait_arrivals for two (request, KV head g) counters at once (b2 < 0: one):
+// each poll loads both, so the two waits cost one round trip, not two.
+template <class A>
+__device__ __forceinline__ void wait_arrivals2(const A& a, int b1, int n1, int b2, int n2, int g) {
+  if (b2 < 0) {
+    wait_arrivals(a, b1, g, n1);
+    return;
+  }
+  int32_t* c1 = a.counters + static_cast<size_t>(b1) * a.n_kv + g;
+  int32_t* c2 = a.counters + static_cast<size_t>(b2) * a.n_kv + g;
+  bool ok1 = false, ok2 = false;
+  for (int it = 0; it < a.spin_limit && !(ok1 && ok2); ++it) {
+    const int32_t v1 = __hip_atomic_load(c1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t v2 = __hip_atomic_load(c2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ok1 = ok1 || v1 >= n1;
+    ok2 = ok2 || v2 >= n2;
+    if (!(ok1 && ok2)) __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok1) ok1 = __hip_atomic_load(c1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n1;
+  if (!ok2) ok2 = __hip_atomic_load(c2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n2;
+  if (!ok1) __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!ok2) __hip_atomic_fetch_add(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(c1, -n1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(c2, -n2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------ timeline
 // Records of gkv_step_trace (see kTraceWords): one thread per workgroup
 // writes its start, a mark and its end.
@@ -1019,7 +1219,18 @@ struct SuffixSmem {
   int32_t ids[kWaves][kWaveTokens];
   float o[kWaves][16][D];
   float lse[kWaves][16];
+  // the merged result of a folded pair's first part, joined at the end of
+  // the pair (suffix joins)
+  float keep_o[16][D];
+  float keep_lse[16];
 };
+
+// What a suffix part does with its four wave results: publish them (the
+// part's partial, counted for its join workgroup, or the request's output),
+// keep their merge in LDS for the workgroup's join at the end of a folded
+// pair (first part), or leave them in LDS for that join (last part).  A
+// request without a HOT prefix is always finished in place.
+enum class PartEnd { kPublish, kKeep, kLeave };
 
 // A wave's piece of one suffix part: the part's request b, the end tb1 of
 // its slot-table range, and the wave's quarter [w0, w0 + len) of the part
@@ -1122,7 +1333,7 @@ __device__ __forceinline__ void suffix_copy_new(const A& a, int b, int gk, int l
 }
 
 template <typename T, int D, typename P, class A>
-__device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_t* smem_raw) {
+__device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_t* smem_raw, PartEnd end) {
   using TR = Traits<T, D>;
   using KOp = typename TR::KOp;
   using VVec = typename TR::VVec;
@@ -1255,6 +1466,25 @@ __device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_
   // the wave pieces meet in LDS
   suffix_to_lds<T, D>(sm, wave, n, g, col_ok, o, lse2);
   __syncthreads();
+  if (end != PartEnd::kPublish && table_at(a.req_class, b) >= 0) {
+    if (end == PartEnd::kKeep) {
+      constexpr int PER = D / 64;
+      for (int col = wave; col < G; col += kWaves) {
+        float acc[PER];
+        const float l2 = join_parts<PER, 4>(
+            kWaves, lane, [&](int p) { return sm.lse[p][col]; },
+            [&](int p, float (&v)[PER]) {
+#pragma unroll
+              for (int j = 0; j < PER; ++j) v[j] = sm.o[p][col][PER * lane + j];
+            },
+            acc);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) sm.keep_o[col][PER * lane + j] = acc[j];
+        if (lane == 0) sm.keep_lse[col] = l2;
+      }
+    }
+    return;
+  }
   if (suffix_publish<T, D, P>(a, sm, part, b, single, gk, wave, lane)) return;
 
   // this part's partial is written: count it for the request's join
@@ -1266,18 +1496,66 @@ __device__ __forceinline__ void suffix_part(const A& a, int part, int gk, uint8_
 // Suffix block i: part q = i / n_kv for KV head i % n_kv, or, folded, part
 // n_parts-1-q (the shorter) and then part q; the barrier between the two
 // frees the LDS.  Folded, blocks q >= ceil(n_parts / 2) are grid padding.
+//
+// Suffix joins (every request's slot table is one part): the workgroup
+// joins its parts' requests itself, for its KV head, once the requests'
+// prefix splits have arrived (a request without a HOT prefix is finished by
+// its part): the first part's merged result waits in LDS, the last part's
+// four wave results are joined directly, and no part partial or join
+// workgroup is needed.  The prefix splits never wait and precede every
+// suffix block in each XCD's in-order dispatch, so the wait ends.
 template <typename T, int D, typename P, class A>
 __device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_raw) {
   const int q = blk / a.n_kv;
   const int gk = blk - q * a.n_kv;
   if (q >= (a.fold ? (a.n_parts + 1) / 2 : a.n_parts)) return;   // grid padding
   const int first = a.fold ? a.n_parts - 1 - q : q;
+  const bool joins = a.suffix_joins != 0;
   if (first > q) {
-    suffix_part<T, D, P>(a, first, gk, smem_raw);
+    suffix_part<T, D, P>(a, first, gk, smem_raw, joins ? PartEnd::kKeep : PartEnd::kPublish);
     __syncthreads();
     trace_mark(a, a.prefix_blocks + blk);
   }
-  suffix_part<T, D, P>(a, q, gk, smem_raw);
+  suffix_part<T, D, P>(a, q, gk, smem_raw, joins ? PartEnd::kLeave : PartEnd::kPublish);
+  if (!joins) return;
+
+  // the parts' requests and their prefix splits (-1: no HOT prefix, done)
+  auto req_of = [&](int part) {
+    const int b = a.ranks[part].req;   // one part per request: part = rank
+    return table_at(a.req_class, b) >= 0 ? b : -1;
+  };
+  const int b_last = req_of(q), b_first = first > q ? req_of(first) : -1;
+  if (b_last < 0 && b_first < 0) return;
+  auto splits_of = [&](int b) { return a.classes[table_at(a.req_class, b)].n_splits; };
+  if (threadIdx.x == 0) {
+    if (b_last >= 0)
+      wait_arrivals2(a, b_last, splits_of(b_last), b_first, b_first >= 0 ? splits_of(b_first) : 0, gk);
+    else
+      wait_arrivals(a, b_first, gk, splits_of(b_first));
+  }
+  __syncthreads();
+  SuffixSmem<T, D>& sm = *reinterpret_cast<SuffixSmem<T, D>*>(smem_raw);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = a.group;
+  const int ns_last = b_last >= 0 ? splits_of(b_last) : 0, ns_first = b_first >= 0 ? splits_of(b_first) : 0;
+  for (int col = wave; col < G; col += kWaves) {
+    const int h = gk * G + col;
+    if (ns_last <= 32 && ns_first <= 32) {
+      // both joins' loads in flight together: one round trip
+      decltype(local_loads<T, D, P>(a, 1, 0, 0, lane)) rl, rf;
+      if (b_last >= 0) rl = local_loads<T, D, P>(a, ns_last, b_last, h, lane);
+      if (b_first >= 0) rf = local_loads<T, D, P>(a, ns_first, b_first, h, lane);
+      if (b_last >= 0)
+        local_finish<T, D, P, kWaves>(a, rl, ns_last, b_last, h, &sm.o[0][col][0], 16 * D, &sm.lse[0][col], 16, lane);
+      if (b_first >= 0)
+        local_finish<T, D, P, 1>(a, rf, ns_first, b_first, h, &sm.keep_o[col][0], D, &sm.keep_lse[col], 1, lane);
+    } else {
+      if (b_last >= 0)
+        join_local<T, D, P, kWaves>(a, ns_last, b_last, h, &sm.o[0][col][0], 16 * D, &sm.lse[0][col], 16, lane);
+      if (b_first >= 0)
+        join_local<T, D, P, 1>(a, ns_first, b_first, h, &sm.keep_o[col][0], D, &sm.keep_lse[col], 1, lane);
+    }
+  }
 }
 
 // ------------------------------------------------------------ prefix kernel
@@ -1895,7 +2173,7 @@ __device__ __forceinline__ void short_join(const A& a, int r0, int nr, int blk) 
 template <typename T, int D, typename P, class A>
 __device__ __forceinline__ void join_block(const A& a, int j) {
   const int blk = a.prefix_blocks + a.suffix_blocks + j;
-  const int nj = a.inline_rank0 * a.n_kv;
+  const int nj = a.suffix_joins ? 0 : a.inline_rank0 * a.n_kv;
   if (j >= nj) {
     const int r0 = a.inline_rank0 + (j - nj) * a.short_per_block;
     short_join<T, D, P>(a, r0, min(a.short_per_block, a.batch - r0), blk);

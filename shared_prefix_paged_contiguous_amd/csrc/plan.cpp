@@ -268,7 +268,11 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   const int32_t n_short = batch - inline_rank0;
   const int32_t short_per = n_short > step_slots ? static_cast<int32_t>(ceil_div(n_short, step_slots)) : 1;
   a.short_per_block = short_per;
-  a.join_blocks = a.need_merge ? inline_rank0 * n_kv + static_cast<int32_t>(ceil_div(n_short, short_per)) : 0;
+  // every slot table is one part: the suffix workgroups join their requests
+  // (see StepArgs), and only the short requests have join workgroups
+  a.suffix_joins = (multi == 0 && parts > 0) ? 1 : 0;
+  const int32_t ranked_joins = a.suffix_joins ? 0 : inline_rank0 * n_kv;
+  a.join_blocks = a.need_merge ? ranked_joins + static_cast<int32_t>(ceil_div(n_short, short_per)) : 0;
   plan.n_short = n_short;
   plan.n_parts = static_cast<int32_t>(parts);
   plan.part_tokens = kSuffixPart;

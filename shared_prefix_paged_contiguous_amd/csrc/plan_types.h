@@ -78,11 +78,14 @@ struct ClassDesc {
 // table positions [j * kSuffixPart, (j+1) * kSuffixPart) and the 4 waves
 // take consecutive quarters of it.  Block i -> part i / n_kv, KV head
 // i % n_kv.  A request with no HOT prefix and one part is finished in the
-// suffix workgroup's epilogue.  Otherwise every prefix split and suffix part
-// writes a partial per (request, query head) and counts its arrival on the
-// (request, KV head) counter; a join workgroup, placed after all prefix and
-// suffix work in the grid, waits for the count and joins the partials into
-// the output.
+// suffix workgroup's epilogue.  Otherwise every prefix split writes a
+// partial per (request, query head) and counts its arrival on the (request,
+// KV head) counter.  When every slot table is one part (suffix_joins), the
+// suffix workgroup that attended a request's part waits for that count and
+// joins the prefix partials with its own result, kept in LDS, into the
+// output.  Otherwise the suffix parts write partials and count arrivals too,
+// and a join workgroup per (request, KV head), placed after all prefix and
+// suffix work in the grid, waits for the count and joins the partials.
 //
 // Folding (cascade steps): when the parts' workgroups would not all fit in
 // the workgroup slots the prefix leaves but half as many would, suffix block
@@ -147,6 +150,7 @@ struct StepHead {
   int32_t partial_f32;         // partial rows are fp32 (else the input dtype)
   int32_t inline_rank0;        // ranks [inline_rank0, batch) are short requests (no suffix part)
   int32_t short_per_block;     // short requests per join workgroup (consecutive ranks)
+  int32_t suffix_joins;        // every slot table is one part: suffix workgroups join their requests
   const void* q;
   void* out;
   float* lse;

@@ -296,14 +296,15 @@ def test_plan_of_the_bench_step():
     of 32 requests = 262144 units over 256 target workgroups gives 1024-token
     splits, 16 per (KV head, M-tile): 256 prefix workgroups.  64 parts x 8 KV
     heads = 512 workgroups overflow the 256 slots left, 32 folded pairs x 8 =
-    256 fit: folded.  One join per (request, KV head): 512."""
+    256 fit: folded.  Every slot table is one part, so the suffix workgroups
+    join their requests themselves: no join workgroups."""
     c = _llama_ctx()
     pid, _ = c.hot_pool_alloc(16384)
     lens = np.random.default_rng(5).integers(128, 1025, size=64)
     indptr = np.concatenate([[0], np.cumsum(lens)])
     p = c.plan_step([pid] * 64, indptr)
     assert p["backend"] == binding.BACKEND_CASCADE and p["m_eff"] == 256 and p["n_classes"] == 1
-    assert (p["n_prefix_blocks"], p["n_suffix_blocks"], p["n_join_blocks"]) == (256, 256, 512)
+    assert (p["n_prefix_blocks"], p["n_suffix_blocks"], p["n_join_blocks"]) == (256, 256, 0)
     assert p["folded_parts"] == 1 and p["n_suffix_parts"] == 64 and p["n_short_requests"] == 0
     assert p["joins_partials"] == 1 and p["workspace_bytes"] > 0
     # the grid does not depend on the order the requests come in

@@ -225,6 +225,23 @@ def test_score_jumps_move_the_reference_points(dtype, force):
         check(out, lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_suffix_joins_with_many_prefix_splits(dtype):
+    """Every slot table is one part, so the suffix workgroups join their
+    requests themselves; a 16K prefix over 2 KV heads and three requests is
+    cut into 64 splits, more than the one-batch join of 32 partials takes,
+    and a suffix-only request and an empty table share the step."""
+    s = spec(n_q=8, n_kv=2, head_dim=128, dtype=dtype, batch=4, prefix_len=16384, hot_capacity=16384,
+             fixed_suffix=(700, 40, 2000, 0))
+    w = workloads.make(s)
+    w.request_prefix[2] = -1          # suffix only: finished by its part
+    st, out, lse, _ = run(w, force=CASCADE)
+    plan = st.ctx.last_plan()
+    assert plan["n_join_blocks"] == 1 and plan["n_short_requests"] == 1   # the empty table is short
+    assert plan["n_prefix_blocks"] >= 2 * 33
+    check(out, lse, *oracle_ref(w), **(FP32_TOL if dtype == "f32" else {}))
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_largest_batch_parity(force):
     """The largest batch one step takes (1024 requests): one shared prefix,
@@ -329,7 +346,8 @@ def test_short_requests_join_their_own_tiles(n_q, n_kv, d, dtype, force):
     st, out, lse, _ = run(w, force=force)
     plan = st.ctx.last_plan()
     assert plan["n_short_requests"] == 7 and plan["n_suffix_parts"] == 1
-    assert plan["n_join_blocks"] == n_kv + 7
+    # the one request with a suffix part is joined by its suffix workgroups
+    assert plan["n_join_blocks"] == 7
     check(out, lse, *oracle_ref(w), **(FP32_TOL if dtype == "f32" else {}))
 
 
