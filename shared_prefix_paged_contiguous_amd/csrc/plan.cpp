@@ -269,8 +269,19 @@ int build_plan(const PlanShape& shape, const HotPool& hot, int32_t batch, const 
   const int32_t short_per = n_short > step_slots ? static_cast<int32_t>(ceil_div(n_short, step_slots)) : 1;
   a.short_per_block = short_per;
   // every slot table is one part: the suffix workgroups join their requests
-  // (see StepArgs), and only the short requests have join workgroups
-  a.suffix_joins = (multi == 0 && parts > 0) ? 1 : 0;
+  // (see StepArgs), and only the short requests have join workgroups.  A
+  // suffix workgroup that joins waits for its requests' prefix splits and
+  // holds its slot meanwhile, so a cascade step does this only when its
+  // prefix and suffix workgroups are all resident at once (a suffix
+  // workgroup waiting on a long prefix would otherwise keep the next round
+  // of suffix work from starting: Llama-3.1-8B shape B = 256, 2048 suffix
+  // workgroups in 7 rounds, 164 -> 196 us).  Dense steps start their
+  // suffix workgroups as the prefix splits end, so their waits are short.
+  a.suffix_joins = (multi == 0 && parts > 0 &&
+                    (backend == GKV_BACKEND_DENSE ||
+                     static_cast<int64_t>(a.prefix_blocks) + a.suffix_blocks <= step_slots))
+                       ? 1
+                       : 0;
   const int32_t ranked_joins = a.suffix_joins ? 0 : inline_rank0 * n_kv;
   a.join_blocks = a.need_merge ? ranked_joins + static_cast<int32_t>(ceil_div(n_short, short_per)) : 0;
   plan.n_short = n_short;
