@@ -60,6 +60,36 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+def resource_usage() -> dict:
+    """Per-kernel resource use of the device code, from the compiler's
+    kernel-resource-usage remarks on a device-only compile of kernels.hip:
+    {mangled kernel name: {"VGPRs": n, "AGPRs": n, "ScratchSize": bytes per
+    lane, "VGPRs Spill": n, "SGPRs Spill": n, "Occupancy": waves per SIMD,
+    "LDS Size": bytes per block, ...}}."""
+    import re
+    import tempfile
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-Wl,-z,defs")],
+               "--cuda-device-only", "-c", "-Rpass-analysis=kernel-resource-usage",
+               "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "kernels.hip"),
+               "-o", os.path.join(tmp, "kernels.o")]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed compiling kernels.hip")
+    usage, name = {}, None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: +Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            usage[name] = {}
+            continue
+        m = re.search(r"remark: +([A-Za-z ]+?)(?: \[[^]]*\])?: (\d+) \[", line)
+        if m and name is not None:
+            usage[name][m.group(1)] = int(m.group(2))
+    return usage
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--verbose", action="store_true")

@@ -1540,8 +1540,9 @@ __device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_
   const int ns_last = b_last >= 0 ? splits_of(b_last) : 0, ns_first = b_first >= 0 ? splits_of(b_first) : 0;
   for (int col = wave; col < G; col += kWaves) {
     const int h = gk * G + col;
-    if (ns_last <= 32 && ns_first <= 32) {
-      // both joins' loads in flight together: one round trip
+    if (sizeof(P) == 2 && ns_last <= 32 && ns_first <= 32) {
+      // both joins' loads in flight together: one round trip (bf16 partials
+      // only: with fp32 rows the two load sets would not fit the registers)
       decltype(local_loads<T, D, P>(a, 1, 0, 0, lane)) rl, rf;
       if (b_last >= 0) rl = local_loads<T, D, P>(a, ns_last, b_last, h, lane);
       if (b_first >= 0) rf = local_loads<T, D, P>(a, ns_first, b_first, h, lane);
