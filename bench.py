@@ -436,11 +436,14 @@ def _median_or_none(xs):
 
 def timeline(args):
     """Per-workgroup timeline of the step kernel (gkv_step_trace) on the
-    bench workload: each workgroup's start, mid-point mark and end from the
-    device's 100 MHz clock, over --tl-steps steps on rotating layer replicas.
-    Reports, per kind of workgroup (prefix split, suffix part or folded pair,
-    join), the percentiles of start, mark and end relative to the first start
-    of the step (microseconds), the kernel span, how many workgroups of each
+    bench workload: each workgroup's start, marks and end from the device's
+    100 MHz clock, over --tl-steps steps on rotating layer replicas.  Reports,
+    per kind of workgroup (prefix split, suffix part or folded pair, join),
+    the percentiles of start, marks and end relative to the first start of
+    the step (microseconds), the per-workgroup lengths of the phases between
+    marks (prefix: partial stores, then arrivals; suffix workgroups that join
+    their own requests: the wait for the prefix splits, then the join), the
+    kernel span, how many workgroups of each
     kind are running in each 2 us bin (median step), and whether each prefix
     workgroup ran on the XCD its index names (index modulo the XCD count)."""
     import torch
@@ -459,7 +462,8 @@ def timeline(args):
     torch.cuda.synchronize()
     plan = st.ctx.last_plan()
     grid = plan["n_prefix_blocks"] + plan["n_suffix_blocks"] + plan["n_join_blocks"]
-    buf = torch.zeros(grid * 4, dtype=torch.int64, device="cuda")
+    words = 8   # per-workgroup record of gkv_step_trace
+    buf = torch.zeros(grid * words, dtype=torch.int64, device="cuda")
     st.ctx.step_trace(buf)
     runs = []
     with no_gc_pauses():
@@ -467,7 +471,7 @@ def timeline(args):
             buf.zero_()
             st.step(out, lse, k_new, v_new, slots, layer=i % replicas)
             torch.cuda.synchronize()
-            runs.append(buf.cpu().numpy().reshape(grid, 4).astype(np.int64))
+            runs.append(buf.cpu().numpy().reshape(grid, words).astype(np.int64))
     st.ctx.step_trace(None)
 
     n_kv = w.spec.n_kv
@@ -489,12 +493,21 @@ def timeline(args):
             if not m.any():
                 continue
             d = {"n": int(m.sum())}
-            for part, col in (("start", 0), ("mark", 1), ("end", 2)):
+            for part, col in (("start", 0), ("mark", 1), ("end", 2), ("mark2", 4), ("mark3", 5)):
                 v = rec[m, col]
                 if part == "mark" and name == "suffix" and not plan["folded_parts"]:
                     continue
+                if part in ("mark2", "mark3") and not (v != 0).all():
+                    continue
                 x = us(v)
                 d[part] = [round(float(np.percentile(x, p)), 2) for p in (0, 50, 100)]
+            # per-workgroup phase lengths between consecutive marks
+            phases = {"prefix": (("epilogue_stores", 1, 4), ("arrivals_to_end", 4, 2)),
+                      "suffix": (("wait", 4, 5), ("join", 5, 2))}.get(name, ())
+            for label, c0, c1 in phases:
+                if (rec[m, c0] != 0).all() and (rec[m, c1] != 0).all():
+                    x = us(rec[m, c1]) - us(rec[m, c0])
+                    d[label + "_us"] = [round(float(np.percentile(x, p)), 2) for p in (0, 50, 90, 100)]
             stats_m = us(rec[m, 2]) - us(rec[m, 0])
             d["duration_p50"] = round(float(np.median(stats_m)), 2)
             row[name] = d
@@ -527,7 +540,10 @@ def timeline(args):
            "span_us_all": sorted(round(r["span_us"], 2) for r in stats), "median_step": med,
            "note": "times in us from the step's first workgroup start (s_memrealtime, 100 MHz); "
                    "[min, median, max] over workgroups; prefix mark = end of the block loop, "
-                   "suffix mark = end of the first part of a folded pair, join mark = end of the wait",
+                   "suffix mark = end of the first part of a folded pair, join mark = end of the wait; "
+                   "mark2 = prefix: partial rows stored (before its arrivals), suffix joining its own "
+                   "requests: end of its tiles; mark3 = that suffix workgroup's end of the wait for its "
+                   "requests' prefix splits; *_us = per-workgroup phase lengths [min, p50, p90, max]",
            "ends_median_over_steps": {k: [_median_or_none([r["ends"][k][i] for r in stats])
                                           for i in range(len(stats[0]["ends"][k]))]
                                       for k in stats[0]["ends"]}}

@@ -413,15 +413,20 @@ int gkv_set_join_spin_limit(gkv_ctx* ctx, int32_t polls);
 
 /* Measurement: per-workgroup timeline of the following step launches of this
  * context.  With trace_dev non-null (dev, 8-byte aligned, `bytes` long) every
- * step whose grid fits (32 bytes per workgroup; the grid is n_prefix_blocks +
+ * step whose grid fits (64 bytes per workgroup; the grid is n_prefix_blocks +
  * n_suffix_blocks + n_join_blocks of gkv_last_plan) writes, per workgroup b,
- * four uint64 at trace_dev[4 b]: its start, a mid-point mark (prefix split:
- * end of its block loop; suffix workgroup: end of its first part when it
- * runs two, else 0; join: end of its wait), its end - s_memrealtime ticks
- * of the 100 MHz clock common to the device - and (kind << 32) | (XCC id
- * << 16) | (low 16 bits of the wave's HW_ID register), kind 0 = prefix,
- * 1 = suffix, 2 = join.  A step whose grid does not fit is not traced.
- * trace_dev NULL turns tracing off.  Host-only. */
+ * eight uint64 at trace_dev[8 b]: [0] its start; [1] a mid-point mark
+ * (prefix split: end of its block loop; suffix workgroup: end of its first
+ * part when it runs two, else 0; join: end of its wait); [2] its end;
+ * [3] (kind << 32) | (XCC id << 16) | (low 16 bits of the wave's HW_ID
+ * register), kind 0 = prefix, 1 = suffix, 2 = join; [4] a second mark
+ * (prefix split: its partial rows stored, before it counts its arrivals;
+ * suffix workgroup joining its own requests: end of its tiles; else 0);
+ * [5] a third mark (suffix workgroup joining its own requests: end of its
+ * wait for their prefix splits; else 0); [6], [7] unused.  Times are
+ * s_memrealtime ticks of the 100 MHz clock common to the device.  A step
+ * whose grid does not fit is not traced.  trace_dev NULL turns tracing off.
+ * Host-only. */
 int gkv_step_trace(gkv_ctx* ctx, void* trace_dev, size_t bytes);
 
 /* Measurement: a plain streaming read of `bytes` (a multiple of 16) at dev

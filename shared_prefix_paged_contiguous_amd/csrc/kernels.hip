@@ -1191,21 +1191,23 @@ __device__ __forceinline__ void wait_arrivals2(const A& a, int b1, int n1, int b
 
 // ------------------------------------------------------------ timeline
 // Records of gkv_step_trace (see kTraceWords): one thread per workgroup
-// writes its start, a mark and its end.
+// writes its start, its marks and its end.
 template <class A>
 __device__ __forceinline__ void trace_start(const A& a, int blk, uint32_t kind) {
   // HW_ID (hardware register 4) and XCC_ID (20), whole 32-bit fields
   const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);
   const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20) & 0xf;
   uint64_t* r = a.trace + static_cast<size_t>(blk) * kTraceWords;
-  r[0] = __builtin_amdgcn_s_memrealtime();
-  r[1] = 0;
-  r[3] = (static_cast<uint64_t>(kind) << 32) | (xcc << 16) | (hw & 0xffff);
+  r[kTraceStart] = __builtin_amdgcn_s_memrealtime();
+  r[kTraceMark] = 0;
+  r[kTraceMark2] = 0;
+  r[kTraceMark3] = 0;
+  r[kTraceKind] = (static_cast<uint64_t>(kind) << 32) | (xcc << 16) | (hw & 0xffff);
 }
 template <class A>
-__device__ __forceinline__ void trace_mark(const A& a, int blk) {
+__device__ __forceinline__ void trace_mark(const A& a, int blk, int word = kTraceMark) {
   if (a.trace && threadIdx.x == 0)
-    a.trace[static_cast<size_t>(blk) * kTraceWords + 1] = __builtin_amdgcn_s_memrealtime();
+    a.trace[static_cast<size_t>(blk) * kTraceWords + word] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ------------------------------------------------------------ suffix blocks
@@ -1518,6 +1520,7 @@ __device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_
   }
   suffix_part<T, D, P>(a, q, gk, smem_raw, joins ? PartEnd::kLeave : PartEnd::kPublish);
   if (!joins) return;
+  trace_mark(a, a.prefix_blocks + blk, kTraceMark2);
 
   // the parts' requests and their prefix splits (-1: no HOT prefix, done)
   auto req_of = [&](int part) {
@@ -1534,6 +1537,7 @@ __device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_
       wait_arrivals(a, b_first, gk, splits_of(b_first));
   }
   __syncthreads();
+  trace_mark(a, a.prefix_blocks + blk, kTraceMark3);
   SuffixSmem<T, D>& sm = *reinterpret_cast<SuffixSmem<T, D>*>(smem_raw);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = a.group;
@@ -1982,6 +1986,7 @@ __device__ __forceinline__ void prefix_block(const A& a, int blk, uint8_t* smem_
   // tile (its G rows for this KV head) for the requests' joins
   wait_stores();
   __syncthreads();
+  trace_mark(a, blk, kTraceMark2);
   if (wave == 0) {
     if (lane < n_mem) arrive(a, mb0, kv_head);
     if (lane + 64 < n_mem) arrive(a, mb1, kv_head);
@@ -2208,7 +2213,7 @@ __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 && D == 128 ? 1 : 2))) void st
   else suffix_block<T, D, P>(a, blk - a.prefix_blocks, smem);
   if (a.trace) {
     __syncthreads();
-    if (threadIdx.x == 0) a.trace[static_cast<size_t>(blk) * kTraceWords + 2] = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) a.trace[static_cast<size_t>(blk) * kTraceWords + kTraceEnd] = __builtin_amdgcn_s_memrealtime();
   }
 }
 

@@ -209,11 +209,18 @@ constexpr int32_t cold_row_pos(int32_t g, int32_t slot, int32_t mask) { return g
 // (their outputs are not valid).  Zero while every step is well formed.
 constexpr int kDefaultSpinLimit = 1 << 16;
 
-// Timeline record of one workgroup (gkv_step_trace): start, a mid-point mark
-// (prefix: end of the block loop; suffix: end of the first part; join: end of
-// its wait), end - all s_memrealtime ticks (100 MHz) - and (kind << 32) | the
-// XCC id << 16 | the low 16 bits of HW_ID (wave, SIMD, CU, SH, SE).
-constexpr int kTraceWords = 4;
+// Timeline record of one workgroup (gkv_step_trace), s_memrealtime ticks
+// (100 MHz) unless noted: start; a mid-point mark (prefix: end of the block
+// loop; suffix: end of the first part of a folded pair; join: end of its
+// wait); end; (kind << 32) | the XCC id << 16 | the low 16 bits of HW_ID
+// (wave, SIMD, CU, SH, SE); a second mark (prefix: its partial rows stored,
+// before the arrivals; suffix with suffix joins: end of its tiles); a third
+// mark (suffix with suffix joins: end of the wait for its requests' prefix
+// splits); two unused words.  Marks a workgroup does not reach stay 0.
+constexpr int kTraceWords = 8;
+enum TraceWord : int {
+  kTraceStart = 0, kTraceMark = 1, kTraceEnd = 2, kTraceKind = 3, kTraceMark2 = 4, kTraceMark3 = 5
+};
 enum TraceKind : uint32_t { kTracePrefix = 0, kTraceSuffix = 1, kTraceJoin = 2 };
 
 // Static scratch of the allocation-free step, per device: a 256-byte status
