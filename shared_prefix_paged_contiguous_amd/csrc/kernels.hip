@@ -984,6 +984,31 @@ __device__ __forceinline__ void local_finish(const A& a, const LocalLoads<NL>& r
     a.lse[static_cast<size_t>(b) * a.n_q + h] = empty ? kNegInf : (mx + __log2f(wsum)) * 0.69314718055994531f;
 }
 
+// One wave's joins of request b (ns <= 32 prefix partials) for the query
+// heads h0 + c, c = c0, c0 + cstep, ... < G, with NL_LOC partials in LDS per
+// head (head c's at loc_o + c * D and loc_lse + c, the NL_LOC of one head
+// o_stride and l_stride apart): three joins' loads are issued before any of
+// them is finished.
+template <typename T, int D, typename P, int NL_LOC, class A>
+__device__ __forceinline__ void local_joins(const A& a, int ns, int b, int h0, int c0, int cstep, int G,
+                                            const float* loc_o, int o_stride, const float* loc_lse, int l_stride,
+                                            int lane) {
+  constexpr int kInFlight = 3;
+  for (int c = c0; c < G; c += kInFlight * cstep) {
+    decltype(local_loads<T, D, P>(a, 1, 0, 0, lane)) r[kInFlight];
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k)
+      if (c + k * cstep < G) r[k] = local_loads<T, D, P>(a, ns, b, h0 + c + k * cstep, lane);
+#pragma unroll
+    for (int k = 0; k < kInFlight; ++k) {
+      const int col = c + k * cstep;
+      if (col < G)
+        local_finish<T, D, P, NL_LOC>(a, r[k], ns, b, h0 + col, loc_o + col * D, o_stride, loc_lse + col, l_stride,
+                                      lane);
+    }
+  }
+}
+
 // Joins the partials of request b for the G query heads of KV head gk, 64 /
 // CH heads per pass: lane l takes 16-byte chunk l % CH of query head
 // gk * G + l / CH and walks the partials itself, NB at a time with all their
@@ -1542,24 +1567,30 @@ __device__ __forceinline__ void suffix_block(const A& a, int blk, uint8_t* smem_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = a.group;
   const int ns_last = b_last >= 0 ? splits_of(b_last) : 0, ns_first = b_first >= 0 ? splits_of(b_first) : 0;
+  if (sizeof(P) == 2 && ns_last <= 32 && ns_first <= 32) {
+    // The G (query head, request) joins of each request are dealt to the
+    // waves in turn; with two requests the even waves take the last part's
+    // and the odd waves the first part's, so a wave's joins are of one kind.
+    // A wave keeps up to three joins' loads in flight (one round trip for
+    // G <= 6; bf16 partials only: fp32 rows would not fit the registers).
+    const bool two = b_last >= 0 && b_first >= 0;
+    const bool of_first = two ? (wave & 1) != 0 : b_last < 0;
+    const int cstep = two ? kWaves / 2 : kWaves;
+    const int c0 = two ? wave >> 1 : wave;
+    if (of_first)
+      local_joins<T, D, P, 1>(a, ns_first, b_first, gk * G, c0, cstep, G, &sm.keep_o[0][0], D, &sm.keep_lse[0], 1,
+                              lane);
+    else
+      local_joins<T, D, P, kWaves>(a, ns_last, b_last, gk * G, c0, cstep, G, &sm.o[0][0][0], 16 * D, &sm.lse[0][0],
+                                   16, lane);
+    return;
+  }
   for (int col = wave; col < G; col += kWaves) {
     const int h = gk * G + col;
-    if (sizeof(P) == 2 && ns_last <= 32 && ns_first <= 32) {
-      // both joins' loads in flight together: one round trip (bf16 partials
-      // only: with fp32 rows the two load sets would not fit the registers)
-      decltype(local_loads<T, D, P>(a, 1, 0, 0, lane)) rl, rf;
-      if (b_last >= 0) rl = local_loads<T, D, P>(a, ns_last, b_last, h, lane);
-      if (b_first >= 0) rf = local_loads<T, D, P>(a, ns_first, b_first, h, lane);
-      if (b_last >= 0)
-        local_finish<T, D, P, kWaves>(a, rl, ns_last, b_last, h, &sm.o[0][col][0], 16 * D, &sm.lse[0][col], 16, lane);
-      if (b_first >= 0)
-        local_finish<T, D, P, 1>(a, rf, ns_first, b_first, h, &sm.keep_o[col][0], D, &sm.keep_lse[col], 1, lane);
-    } else {
-      if (b_last >= 0)
-        join_local<T, D, P, kWaves>(a, ns_last, b_last, h, &sm.o[0][col][0], 16 * D, &sm.lse[0][col], 16, lane);
-      if (b_first >= 0)
-        join_local<T, D, P, 1>(a, ns_first, b_first, h, &sm.keep_o[col][0], D, &sm.keep_lse[col], 1, lane);
-    }
+    if (b_last >= 0)
+      join_local<T, D, P, kWaves>(a, ns_last, b_last, h, &sm.o[0][col][0], 16 * D, &sm.lse[0][col], 16, lane);
+    if (b_first >= 0)
+      join_local<T, D, P, 1>(a, ns_first, b_first, h, &sm.keep_o[col][0], D, &sm.keep_lse[col], 1, lane);
   }
 }
 

@@ -242,6 +242,27 @@ def test_suffix_joins_with_many_prefix_splits(dtype):
     check(out, lse, *oracle_ref(w), **(FP32_TOL if dtype == "f32" else {}))
 
 
+@pytest.mark.parametrize("group", [1, 5, 6, 8, 16])
+def test_suffix_joins_deal_heads_over_waves(group):
+    """Suffix workgroups that join their own requests deal the (query head,
+    request) joins over their four waves, each wave holding up to three
+    joins' loads at once: G = 1 (two waves idle), 5 and 6 (one round), 8 and
+    16 (two rounds).  The 64 requests fold into pairs; two of them have no
+    HOT prefix, so their pairs join one request."""
+    lens = tuple(100 + (i * 53) % 700 for i in range(64))
+    s = spec(n_q=8 * group, n_kv=8, head_dim=128, batch=64, prefix_len=2048, hot_capacity=2048,
+             fixed_suffix=lens, cold_capacity=65536)
+    w = workloads.make(s)
+    w.request_prefix[5] = -1
+    w.request_prefix[40] = -1
+    st, out, lse, _ = run(w, force=CASCADE)
+    plan = st.ctx.last_plan()
+    # folded pairs, every slot table one part, no short request: the suffix
+    # workgroups do every join (no join workgroups)
+    assert plan["folded_parts"] == 1 and plan["n_short_requests"] == 0 and plan["n_join_blocks"] == 0
+    check(out, lse, *oracle_ref(w))
+
+
 @pytest.mark.parametrize("force", [CASCADE, DENSE])
 def test_largest_batch_parity(force):
     """The largest batch one step takes (1024 requests): one shared prefix,
